@@ -1,0 +1,57 @@
+"""Workload shapes: OPT-shaped decoder stacks and the generation sizes run on them.
+
+The pages measure OPT models at prompt 512 / 32 generated tokens with an effective
+batch of 144 = 48 x 3 for the 4-bit weight + KV configuration (FlexGen article,
+section 5.1 and the --gpu-batch-size/--num-gpu-batches flags of section 2.3).
+Vocabulary 50272 and learned positions with an offset of 2 are the OPT conventions.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+VOCAB = 50272
+POS_ROWS = 2050          # 2048 learned positions + the OPT offset of 2
+POS_OFFSET = 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    layers: int
+    hidden: int
+    heads: int
+    ffn: int
+    batch: int
+    prompt: int
+    gen: int                 # generated tokens (1 from prefill + gen-1 decode steps)
+    micro_batch: int         # prefill micro-batch (rows of the batch per prefill call)
+    full_model: bool = True  # False: lone decoder layer fed with N(0,1) activations
+    vocab: int = VOCAB
+
+    @property
+    def head_dim(self) -> int:
+        return self.hidden // self.heads
+
+    @property
+    def max_len(self) -> int:
+        # the last decode step writes position prompt + gen - 2; full models also
+        # keep one more slot so that the cache covers every generated token
+        return self.prompt + self.gen - 1 if self.full_model else self.prompt + self.gen
+
+
+WORKLOADS = {
+    # one OPT-125m-shaped layer, batch 4, prompt 128, then 8 decode steps
+    "opt125m-layer": Workload("opt125m-layer", 1, 768, 12, 3072, 4, 128, 8, 4, full_model=False),
+    # OPT-1.3B shape, batch 32, prompt 512, 32 generated tokens
+    "opt1.3b": Workload("opt1.3b", 24, 2048, 32, 8192, 32, 512, 32, 32),
+    # OPT-30B shape, batch 144 = 3 x 48, prompt 512, 32 generated tokens
+    "opt30b": Workload("opt30b", 48, 7168, 56, 28672, 144, 512, 32, 48),
+    # OPT-175B shape, batch 144 = 3 x 48, prompt 512, 32 generated tokens
+    "opt175b": Workload("opt175b", 96, 12288, 96, 49152, 144, 512, 32, 48),
+}
+
+# KV-compression stress: OPT-30B attention only, batch 64, prompt 2048, 64 decode steps
+KV_STRESS = dict(batch=64, heads=56, head_dim=128, prompt=2048, steps=64,
+                 outlier_frac=0.01, outlier_factor=8.0)
+# standalone quantize of a 4 GiB fp16 tensor (2^31 elements)
+QUANT_4GIB = dict(rows=524288, cols=4096)
