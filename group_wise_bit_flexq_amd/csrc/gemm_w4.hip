@@ -1,0 +1,350 @@
+// Dequant-fused 4-bit-weight GEMM on gfx950 MFMA:  y = x . W^T (+ epilogue).
+//
+// The pages' linear layers are fp16 matmuls whose weights are stored compressed
+// (FlexGen walkthrough, section 6.3: weights grouped along the input dimension,
+// 64 per group, 4 bits, fp16 parameters).  Here the weight tile is expanded to fp16
+// on its way into LDS, once per work-group and k-step, and reused by every row of
+// the work-group's M tile:
+//
+//   x  fp16 [M][K]         --global-->  LDS A tile  [BM][64]
+//   W  codes [N][K/2] + (offset, scale) per 64  --dequant (v_pk_fma_f16)-->  LDS B tile [BN][64]
+//   v_mfma_f32_32x32x16_f16  (fp16 operands, fp32 accumulators)
+//
+// LDS rows are 128 B (one 64-element quantization group); 16-B chunk c of row r
+// lives at chunk c ^ (r & 7) so that 32 lanes reading 32 rows at one k offset hit
+// distinct banks.  Two LDS stages: the next tile's global loads are in flight while
+// the current tile feeds the MFMAs.  Work-groups are 256 threads (4 waves); the
+// wave grid WM x WN and per-wave 32x32 tile counts TM x TN set the block tile.
+// Split-K writes fp32 partial sums that a second kernel adds in split order.
+#include "common.h"
+
+namespace flexq {
+
+constexpr int kBK = 64;
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kBK + ((chunk ^ (row & 7)) << 3);  // in fp16 elements
+}
+
+enum OutKind { kOutF16 = 0, kOutF32 = 1, kOutPartial = 2 };
+
+template <int WM, int WN, int TM, int TN>
+struct GemmShape {
+  static constexpr int BM = WM * TM * 32;
+  static constexpr int BN = WN * TN * 32;
+  static constexpr int THREADS = WM * WN * 64;
+  static constexpr int A_CHUNKS = BM * 8;      // 16-B pieces of an A tile
+  static constexpr int B_PIECES = BN * 2;      // 16-B code pieces (32 codes) of a B tile
+  static constexpr int A_PER_T = A_CHUNKS / THREADS;
+  static constexpr int B_PER_T = (B_PIECES + THREADS - 1) / THREADS;
+  static constexpr size_t LDS_BYTES = 2 * (size_t)(BM + BN) * kBK * sizeof(f16);
+  static_assert(A_CHUNKS % THREADS == 0, "A tile must split evenly over threads");
+};
+
+struct Epilogue {
+  const f16* bias;      // [N] or null
+  const f16* residual;  // [M][N] or null
+  int relu;
+};
+
+__device__ __forceinline__ float epilogue_value(float v, const Epilogue& ep, int64_t row, int col,
+                                                int N) {
+  if (ep.bias) v += (float)ep.bias[col];
+  if (ep.relu) v = fmaxf(v, 0.0f);
+  if (ep.residual) v += (float)ep.residual[row * N + col];
+  return v;
+}
+
+template <int WM, int WN, int TM, int TN, int OUT>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
+    const f16* __restrict__ X, const uint8_t* __restrict__ Wc, const uint32_t* __restrict__ Wp,
+    int M, int N, int K, int kt_per_split, Epilogue ep, void* __restrict__ Y) {
+  using S = GemmShape<WM, WN, TM, TN>;
+  extern __shared__ __attribute__((aligned(16))) f16 smem[];
+  f16* sA = smem;                       // [2][BM*64]
+  f16* sB = smem + 2 * S::BM * kBK;     // [2][BN*64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = blockIdx.y * S::BM;
+  const int n0 = blockIdx.x * S::BN;
+  const int KT = K / kBK;
+  const int kt0 = blockIdx.z * kt_per_split;
+  const int kt1 = min(KT, kt0 + kt_per_split);
+  const int64_t ldc = K / 2, ldp = K / kBK;
+
+  uint4 ra[S::A_PER_T];
+  uint4 rb[S::B_PER_T];
+  uint32_t rp[S::B_PER_T];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < S::A_PER_T; ++j) {
+      const int idx = tid + j * S::THREADS;
+      const int row = idx >> 3, ch = idx & 7;
+      const int gm = m0 + row;
+      ra[j] = gm < M ? *(const uint4*)(X + (int64_t)gm * K + kt * kBK + ch * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < S::B_PER_T; ++j) {
+      const int idx = tid + j * S::THREADS;
+      const int row = idx >> 1, half = idx & 1;
+      const int gn = n0 + row;
+      if (idx < S::B_PIECES && gn < N) {
+        rb[j] = *(const uint4*)(Wc + (int64_t)gn * ldc + kt * 32 + half * 16);
+        rp[j] = Wp[(int64_t)gn * ldp + kt];
+      } else {
+        rb[j] = make_uint4(0, 0, 0, 0);
+        rp[j] = 0;
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    f16* a = sA + buf * S::BM * kBK;
+    f16* b = sB + buf * S::BN * kBK;
+#pragma unroll
+    for (int j = 0; j < S::A_PER_T; ++j) {
+      const int idx = tid + j * S::THREADS;
+      *(uint4*)(a + lds_off(idx >> 3, idx & 7)) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < S::B_PER_T; ++j) {
+      const int idx = tid + j * S::THREADS;
+      if (idx < S::B_PIECES) {
+        const int row = idx >> 1, half = idx & 1;
+        const f16x2 m2 = h2_from_u32((rp[j] & 0xFFFFu) * 0x10001u);
+        const f16x2 s2 = h2_from_u32((rp[j] >> 16) * 0x10001u);
+        const uint32_t w[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t pr[4];
+          codes_to_magic_pairs(w[q], pr);
+          uint4 o;
+          o.x = u32_from_h2(dequant_pair(pr[0], s2, m2));
+          o.y = u32_from_h2(dequant_pair(pr[1], s2, m2));
+          o.z = u32_from_h2(dequant_pair(pr[2], s2, m2));
+          o.w = u32_from_h2(dequant_pair(pr[3], s2, m2));
+          *(uint4*)(b + lds_off(row, half * 4 + q)) = o;
+        }
+      }
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
+
+  if (kt0 < kt1) {
+    load_tile(kt0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) load_tile(kt + 1);
+    const f16* a = sA + buf * S::BM * kBK;
+    const f16* b = sB + buf * S::BN * kBK;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      f16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *(const f16x8*)(a + lds_off(wm * TM * 32 + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[j] = *(const f16x8*)(b + lds_off(wn * TN * 32 + j * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator (i, j, r) of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of tile (i, j)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * TN * 32 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M && col < N) {
+          const float v = acc[i][j][r];
+          if constexpr (OUT == kOutF16) {
+            ((f16*)Y)[(int64_t)row * N + col] = (f16)epilogue_value(v, ep, row, col, N);
+          } else if constexpr (OUT == kOutF32) {
+            ((float*)Y)[(int64_t)row * N + col] = v;
+          } else {
+            ((float*)Y)[((int64_t)blockIdx.z * M + row) * N + col] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Sum of split-K partials in split order, then the epilogue.  4 elements per thread.
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int M, int N, Epilogue ep,
+                                                            void* __restrict__ Y) {
+  const int64_t total = (int64_t)M * N;
+  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= total) return;
+  float v[4] = {0, 0, 0, 0};
+  for (int z = 0; z < splits; ++z) {
+    const float4 p = *(const float4*)(part + (int64_t)z * total + i4);
+    v[0] += p.x;
+    v[1] += p.y;
+    v[2] += p.z;
+    v[3] += p.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t idx = i4 + e;
+    const int64_t row = idx / N;
+    const int col = (int)(idx - row * N);
+    if constexpr (OUT == kOutF16)
+      ((f16*)Y)[idx] = (f16)epilogue_value(v[e], ep, row, col, N);
+    else
+      ((float*)Y)[idx] = v[e];
+  }
+}
+
+// ------------------------------------------------------------------ host dispatch
+
+struct Plan {
+  int cfg;      // which tile shape
+  int bm, bn;
+  int splits;
+  int kt_per_split;
+};
+
+constexpr int kCfgPrefill = 0;  // 128 x 128, 2x2 waves of 64x64
+constexpr int kCfgM32 = 1;      // 32 x 128
+constexpr int kCfgM64 = 2;      // 64 x 128
+constexpr int kCfgM160 = 3;     // 160 x 128
+
+static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
+  Plan p;
+  if (M <= 32) { p.cfg = kCfgM32; p.bm = 32; p.bn = 128; }
+  else if (M <= 64) { p.cfg = kCfgM64; p.bm = 64; p.bn = 128; }
+  else if (M <= 160) { p.cfg = kCfgM160; p.bm = 160; p.bn = 128; }
+  else { p.cfg = kCfgPrefill; p.bm = 128; p.bn = 128; }
+  const int64_t KT = K / kBK;
+  const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+  int splits = 1;
+  // too few work-groups for 256 CUs: split K (fixed rule, so results only depend on
+  // the shape and on whether the workspace is large enough)
+  if (tiles < 512) {
+    splits = (int)((512 + tiles - 1) / tiles);
+    splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, KT / 8));
+    splits = std::min(splits, 16);
+  }
+  if ((M * N) % 4) splits = 1;
+  while (splits > 1 && (size_t)splits * M * N * sizeof(float) > ws_bytes) --splits;
+  p.splits = splits;
+  p.kt_per_split = (int)((KT + splits - 1) / splits);
+  p.splits = (int)((KT + p.kt_per_split - 1) / p.kt_per_split);
+  return p;
+}
+
+template <int WM, int WN, int TM, int TN, int OUT>
+static void launch_cfg(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
+                       void* Y, hipStream_t stream) {
+  using S = GemmShape<WM, WN, TM, TN>;
+  auto kern = gemm_w4_kernel<WM, WN, TM, TN, OUT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)S::LDS_BYTES);
+    attr_set = true;
+  }
+  const int N = (int)W->rows, K = (int)W->cols;
+  dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM, p.splits);
+  hipLaunchKernelGGL(kern, grid, dim3(S::THREADS), S::LDS_BYTES, stream, x, W->codes,
+                     (const uint32_t*)W->params, M, N, K, p.kt_per_split, ep, Y);
+}
+
+template <int OUT>
+static void launch_plan(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
+                        void* Y, hipStream_t stream) {
+  switch (p.cfg) {
+    case kCfgM32: launch_cfg<1, 4, 1, 1, OUT>(p, x, W, M, ep, Y, stream); break;
+    case kCfgM64: launch_cfg<1, 4, 2, 1, OUT>(p, x, W, M, ep, Y, stream); break;
+    case kCfgM160: launch_cfg<1, 4, 5, 1, OUT>(p, x, W, M, ep, Y, stream); break;
+    default: launch_cfg<2, 2, 2, 2, OUT>(p, x, W, M, ep, Y, stream); break;
+  }
+}
+
+static int check_w4(const flexq_w4* W) {
+  if (!W || !W->codes || !W->params) return FLEXQ_ERR_INVALID;
+  if (W->rows <= 0 || W->cols <= 0 || W->cols % kBK) return FLEXQ_ERR_INVALID;
+  if (W->rows > 0x7FFFFFFF || W->cols > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
+  if (((uintptr_t)W->codes & 15) || ((uintptr_t)W->params & 3)) return FLEXQ_ERR_INVALID;
+  return FLEXQ_OK;
+}
+
+static int run_linear(const uint16_t* x, int64_t M, const flexq_w4* W, Epilogue ep, int out_kind,
+                      void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_w4(W);
+  if (st != FLEXQ_OK) return st;
+  if (M < 0 || M > 0x7FFFFFFF) return FLEXQ_ERR_INVALID;
+  if (M == 0) return FLEXQ_OK;
+  if (!x || !y || ((uintptr_t)x & 15)) return FLEXQ_ERR_INVALID;
+  const Plan p = make_plan(M, W->rows, W->cols, ws ? ws_bytes : 0);
+  const f16* xh = (const f16*)x;
+  if (p.splits == 1) {
+    if (out_kind == kOutF16) launch_plan<kOutF16>(p, xh, W, (int)M, ep, y, stream);
+    else launch_plan<kOutF32>(p, xh, W, (int)M, ep, y, stream);
+  } else {
+    const int64_t total = M * W->rows;
+    if (((uintptr_t)ws & 15) || total % 4) return FLEXQ_ERR_INVALID;
+    launch_plan<kOutPartial>(p, xh, W, (int)M, ep, ws, stream);
+    const int64_t blocks = (total / 4 + 255) / 256;
+    if (out_kind == kOutF16)
+      hipLaunchKernelGGL(splitk_reduce_kernel<kOutF16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const float*)ws, p.splits, (int)M, (int)W->rows, ep, y);
+    else
+      hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const float*)ws, p.splits, (int)M, (int)W->rows, ep, y);
+  }
+  FLEXQ_LAUNCH_CHECK();
+  return FLEXQ_OK;
+}
+
+}  // namespace flexq
+
+using namespace flexq;
+
+extern "C" size_t flexq_linear_w4_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % kBK) return 0;
+  const Plan p = make_plan(M, N, K, (size_t)-1);
+  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+}
+
+extern "C" int flexq_linear_w4(const uint16_t* x, int64_t M, const flexq_w4* W, const uint16_t* bias,
+                               const uint16_t* residual, int32_t relu, uint16_t* y, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  Epilogue ep{(const f16*)bias, (const f16*)residual, relu ? 1 : 0};
+  return run_linear(x, M, W, ep, kOutF16, y, ws, ws_bytes, stream);
+}
+
+extern "C" int flexq_linear_w4_f32(const uint16_t* x, int64_t M, const flexq_w4* W, float* y32,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  Epilogue ep{nullptr, nullptr, 0};
+  return run_linear(x, M, W, ep, kOutF32, y32, ws, ws_bytes, stream);
+}

@@ -1,0 +1,192 @@
+// Row kernels around the GEMMs: LayerNorm, token + position embedding
+// (`opt_input_embed`), greedy argmax over logits (`opt_output_embed`'s pick);
+// source notes, section "Pytorch Backend".  All HBM-bound and small next to the
+// GEMMs and attention.
+#include "common.h"
+
+namespace flexq {
+
+constexpr int kLnThreads = 256;
+constexpr int kLnMaxChunks = 8;  // 8 x 256 x 8 = 16384 >= every hidden size here
+
+// One work-group per row; the row stays in registers between the two passes.
+__global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const f16* __restrict__ x,
+                                                               int64_t x_stride, int h,
+                                                               const f16* __restrict__ g,
+                                                               const f16* __restrict__ b,
+                                                               f16* __restrict__ y) {
+  __shared__ float red[8];
+  const int64_t row = blockIdx.x;
+  const f16* xr = x + row * x_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = h / 8;
+  f16x8 v[kLnMaxChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    const int c = tid + i * kLnThreads;
+    if (c < nch) {
+      v[i] = *(const f16x8*)(xr + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)v[i][e];
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const float mean = ((red[0] + red[1]) + (red[2] + red[3])) / (float)h;
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    const int c = tid + i * kLnThreads;
+    if (c < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = (float)v[i][e] - mean;
+        q += d * d;
+      }
+    }
+  }
+  q = wave_sum(q);
+  if (lane == 0) red[4 + wave] = q;
+  __syncthreads();
+  const float var = ((red[4] + red[5]) + (red[6] + red[7])) / (float)h;
+  const float rstd = 1.0f / sqrtf(var + 1e-5f);
+  f16* yr = y + row * h;
+#pragma unroll
+  for (int i = 0; i < kLnMaxChunks; ++i) {
+    const int c = tid + i * kLnThreads;
+    if (c < nch) {
+      const f16x8 gg = *(const f16x8*)(g + c * 8);
+      const f16x8 bb = *(const f16x8*)(b + c * 8);
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = (f16)(((float)v[i][e] - mean) * rstd * (float)gg[e] + (float)bb[e]);
+      *(f16x8*)(yr + c * 8) = o;
+    }
+  }
+}
+
+// out[m][k] = fp16(fp16(c * s + off) + pos[p + 2][k]) with p = pos_base + m % seq.
+// One work-group per row, 16 elements per thread and step.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    int pos_base, int seq, int h,
+                                                    const uint2* __restrict__ codes,
+                                                    const uint32_t* __restrict__ params,
+                                                    const f16* __restrict__ pos, int pos_rows,
+                                                    int vocab, f16* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  int tok = tokens[m];
+  tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
+  int p = pos_base + (int)(m % seq) + 2;
+  p = p >= pos_rows ? pos_rows - 1 : p;
+  for (int c = threadIdx.x; c < h / 16; c += blockDim.x) {
+    const uint2 cw = codes[(int64_t)tok * (h / 16) + c];
+    const uint32_t prm = params[(int64_t)tok * (h / 64) + c / 4];
+    const f16x2 m2 = h2_from_u32((prm & 0xFFFFu) * 0x10001u);
+    const f16x2 s2 = h2_from_u32((prm >> 16) * 0x10001u);
+    uint32_t pr[8];
+    codes_to_magic_pairs(cw.x, pr);
+    codes_to_magic_pairs(cw.y, pr + 4);
+    const f16x8* pp = (const f16x8*)(pos + (int64_t)p * h + c * 16);
+    const f16x8 p0 = pp[0], p1 = pp[1];
+    f16x8 o0, o1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x2 a = dequant_pair(pr[k], s2, m2);
+      const f16x2 bb = dequant_pair(pr[4 + k], s2, m2);
+      o0[2 * k] = (f16)((float)a.x + (float)p0[2 * k]);
+      o0[2 * k + 1] = (f16)((float)a.y + (float)p0[2 * k + 1]);
+      o1[2 * k] = (f16)((float)bb.x + (float)p1[2 * k]);
+      o1[2 * k + 1] = (f16)((float)bb.y + (float)p1[2 * k + 1]);
+    }
+    f16x8* op = (f16x8*)(out + m * h + c * 16);
+    op[0] = o0;
+    op[1] = o1;
+  }
+}
+
+__device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// One work-group per row: largest logit, lowest index among equal maxima.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int64_t N,
+                                                     int32_t* __restrict__ next) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const float* r = logits + (int64_t)blockIdx.x * N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int64_t n = tid; n < N; n += 256) better(bv, bi, r[n], (int)n);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    better(bv, bi, v2, i2);
+  }
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+    next[blockIdx.x] = bi == 0x7FFFFFFF ? 0 : bi;
+  }
+}
+
+}  // namespace flexq
+
+using namespace flexq;
+
+extern "C" int flexq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64_t x_row_stride,
+                               const uint16_t* g, const uint16_t* b, uint16_t* y,
+                               hipStream_t stream) {
+  if (M < 0 || h <= 0 || h % 8 || h > (int64_t)kLnThreads * 8 * kLnMaxChunks) return FLEXQ_ERR_INVALID;
+  if (x_row_stride < h || x_row_stride % 8) return FLEXQ_ERR_INVALID;
+  if (M == 0) return FLEXQ_OK;
+  if (!x || !g || !b || !y) return FLEXQ_ERR_INVALID;
+  if (((uintptr_t)x | (uintptr_t)g | (uintptr_t)b | (uintptr_t)y) & 15) return FLEXQ_ERR_INVALID;
+  if (M > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(layernorm_kernel, dim3((unsigned)M), dim3(kLnThreads), 0, stream, (const f16*)x,
+                     x_row_stride, (int)h, (const f16*)g, (const f16*)b, (f16*)y);
+  FLEXQ_LAUNCH_CHECK();
+  return FLEXQ_OK;
+}
+
+extern "C" int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, int32_t seq,
+                           const flexq_w4* embed, const uint16_t* pos, int32_t pos_rows,
+                           uint16_t* out, hipStream_t stream) {
+  if (n < 0 || !embed || seq <= 0 || pos_base < 0) return FLEXQ_ERR_INVALID;
+  if (n == 0) return FLEXQ_OK;
+  if (!tokens || !embed->codes || !embed->params || !pos || !out) return FLEXQ_ERR_INVALID;
+  const int64_t h = embed->cols;
+  if (h <= 0 || h % 64 || embed->rows <= 0) return FLEXQ_ERR_INVALID;
+  if ((int64_t)pos_base + (n < seq ? n : seq) - 1 + 2 >= pos_rows) return FLEXQ_ERR_INVALID;
+  if (((uintptr_t)embed->codes & 7) || ((uintptr_t)embed->params & 3) || ((uintptr_t)pos & 15) ||
+      ((uintptr_t)out & 15))
+    return FLEXQ_ERR_INVALID;
+  if (n > 0x7FFFFFFF || embed->rows > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)n), dim3(256), 0, stream, tokens, pos_base, seq,
+                     (int)h, (const uint2*)embed->codes, (const uint32_t*)embed->params,
+                     (const f16*)pos, pos_rows, (int)embed->rows, (f16*)out);
+  FLEXQ_LAUNCH_CHECK();
+  return FLEXQ_OK;
+}
+
+extern "C" int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next,
+                            hipStream_t stream) {
+  if (M < 0 || N <= 0 || N > 0x7FFFFFFF) return FLEXQ_ERR_INVALID;
+  if (M == 0) return FLEXQ_OK;
+  if (!logits || !next) return FLEXQ_ERR_INVALID;
+  if (M > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)M), dim3(256), 0, stream, logits, N, next);
+  FLEXQ_LAUNCH_CHECK();
+  return FLEXQ_OK;
+}

@@ -1,0 +1,407 @@
+"""Python binding of libflexq.so (include/flexq.h): argument marshalling only.
+
+Device memory and streams come from PyTorch; every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflexq.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3
+
+EXPORTED = (
+    "flexq_status_string", "flexq_quantize", "flexq_dequantize", "flexq_layernorm",
+    "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
+    "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
+    "flexq_embed", "flexq_argmax", "flexq_layer_workspace_size", "flexq_prefill_layer",
+    "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
+)
+
+
+class FlexqError(RuntimeError):
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name} failed: {msg} ({status})")
+        self.status = status
+
+
+# ------------------------------------------------------------------ C structs
+
+class QConfig(C.Structure):
+    _fields_ = [("num_bits", C.c_int32), ("group_size", C.c_int32), ("symmetric", C.c_int32)]
+
+
+class W4Struct(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("params", C.c_void_p), ("rows", C.c_int64),
+                ("cols", C.c_int64)]
+
+
+class KV4Struct(C.Structure):
+    _fields_ = [("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_params", C.c_void_p),
+                ("v_params", C.c_void_p), ("batch", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("max_len", C.c_int32)]
+
+
+class LayerStruct(C.Structure):
+    _fields_ = [("ln1_g", C.c_void_p), ("ln1_b", C.c_void_p), ("wqkv", W4Struct),
+                ("bqkv", C.c_void_p), ("wo", W4Struct), ("bo", C.c_void_p),
+                ("ln2_g", C.c_void_p), ("ln2_b", C.c_void_p), ("w1", W4Struct),
+                ("b1", C.c_void_p), ("w2", W4Struct), ("b2", C.c_void_p)]
+
+
+class TraceStruct(C.Structure):
+    _fields_ = [("events", C.POINTER(C.c_void_p)), ("kinds", C.POINTER(C.c_int32)),
+                ("rows", C.POINTER(C.c_int64)), ("capacity", C.c_int32), ("count", C.c_int32)]
+
+
+class ModelStruct(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
+                ("ffn", C.c_int32), ("vocab", C.c_int32), ("pos_rows", C.c_int32),
+                ("layer", C.POINTER(LayerStruct)), ("kv", C.POINTER(KV4Struct)),
+                ("embed", W4Struct), ("pos", C.c_void_p), ("lnf_g", C.c_void_p),
+                ("lnf_b", C.c_void_p), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libflexq.so (after torch, so that torch's HIP runtime is the one in use)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                "g.build()'` (or python group_wise_bit_flexq_amd/build.py)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        sig = {
+            "flexq_status_string": (C.c_char_p, [C.c_int]),
+            "flexq_quantize": (C.c_int, [vp, i64, i64, QConfig, vp, vp, vp]),
+            "flexq_dequantize": (C.c_int, [vp, vp, i64, i64, vp, vp]),
+            "flexq_layernorm": (C.c_int, [vp, i64, i64, i64, vp, vp, vp, vp]),
+            "flexq_linear_w4_workspace_size": (sz, [i64, i64, i64]),
+            "flexq_linear_w4": (C.c_int, [vp, i64, C.POINTER(W4Struct), vp, vp, i32, vp, vp, sz, vp]),
+            "flexq_linear_w4_f32": (C.c_int, [vp, i64, C.POINTER(W4Struct), vp, vp, sz, vp]),
+            "flexq_attn_prefill": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct), vp, vp]),
+            "flexq_attn_decode_workspace_size": (sz, [i32, i32, i32, i32]),
+            "flexq_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct), vp, vp,
+                                                sz, vp]),
+            "flexq_embed": (C.c_int, [vp, i64, i32, i32, C.POINTER(W4Struct), vp, i32, vp, vp]),
+            "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
+            "flexq_layer_workspace_size": (sz, [i32, i32, i32, i64, i32]),
+            "flexq_prefill_layer": (C.c_int, [C.POINTER(LayerStruct), C.POINTER(KV4Struct), i32,
+                                              i32, i32, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "flexq_decode_layer": (C.c_int, [C.POINTER(LayerStruct), C.POINTER(KV4Struct), i32,
+                                             i32, i32, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "flexq_model_workspace_size": (sz, [i32, i32, i32, i32, i64, i32, i32]),
+            "flexq_prefill": (C.c_int, [C.POINTER(ModelStruct), vp, i32, i32, i32, vp, vp, vp]),
+            "flexq_decode_step": (C.c_int, [C.POINTER(ModelStruct), vp, i32, i32, vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(name, status):
+    if status != OK:
+        msg = lib().flexq_status_string(status).decode()
+        raise FlexqError(name, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} CUDA tensor")
+
+
+# ------------------------------------------------------------------ compressed tensors
+
+class W4:
+    """A 4-bit weight [rows][cols]: codes uint8 [rows][cols/2], params fp16 [rows][cols/64][2]."""
+
+    def __init__(self, codes: torch.Tensor, params: torch.Tensor):
+        self.codes, self.params = codes, params
+        self.rows, self.cols = codes.shape[0], codes.shape[1] * 2
+
+    def c(self) -> W4Struct:
+        return W4Struct(self.codes.data_ptr(), self.params.data_ptr(), self.rows, self.cols)
+
+    @staticmethod
+    def empty(rows, cols, device="cuda"):
+        return W4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=device),
+                  torch.empty(rows, cols // 64, 2, dtype=torch.float16, device=device))
+
+    def nbytes(self):
+        return self.codes.numel() + self.params.numel() * 2
+
+
+class KV4:
+    """The 4-bit KV cache of one layer (see flexq_kv4_layer)."""
+
+    def __init__(self, batch, heads, head_dim, max_len, device="cuda"):
+        self.batch, self.heads, self.head_dim, self.max_len = batch, heads, head_dim, max_len
+        shp = (batch, heads, max_len, head_dim // 2)
+        pshp = (batch, heads, max_len, head_dim // 64, 2)
+        self.k_codes = torch.zeros(shp, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(shp, dtype=torch.uint8, device=device)
+        self.k_params = torch.zeros(pshp, dtype=torch.float16, device=device)
+        self.v_params = torch.zeros(pshp, dtype=torch.float16, device=device)
+
+    def c(self) -> KV4Struct:
+        return KV4Struct(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+                         self.k_params.data_ptr(), self.v_params.data_ptr(), self.batch,
+                         self.heads, self.head_dim, self.max_len)
+
+    def nbytes(self):
+        return 2 * (self.k_codes.numel() + self.k_params.numel() * 2)
+
+
+# ------------------------------------------------------------------ single calls
+
+QCFG = QConfig(4, 64, 0)
+
+
+def quantize(x: torch.Tensor, out: W4 | None = None, stream=None) -> W4:
+    _need(x, torch.float16, "x")
+    rows = x.numel() // x.shape[-1]
+    cols = x.shape[-1]
+    w = out if out is not None else W4.empty(rows, cols, x.device)
+    _check("flexq_quantize", lib().flexq_quantize(x.data_ptr(), rows, cols, QCFG,
+                                                  w.codes.data_ptr(), w.params.data_ptr(),
+                                                  _stream(stream)))
+    return w
+
+
+def dequantize(w: W4, stream=None) -> torch.Tensor:
+    out = torch.empty(w.rows, w.cols, dtype=torch.float16, device=w.codes.device)
+    _check("flexq_dequantize", lib().flexq_dequantize(w.codes.data_ptr(), w.params.data_ptr(),
+                                                      w.rows, w.cols, out.data_ptr(),
+                                                      _stream(stream)))
+    return out
+
+
+def layernorm(x, g, b, rows=None, row_stride=None, out=None, stream=None):
+    h = g.numel()
+    M = rows if rows is not None else x.numel() // h
+    stride = row_stride if row_stride is not None else h
+    y = out if out is not None else torch.empty(M, h, dtype=torch.float16, device=x.device)
+    _check("flexq_layernorm", lib().flexq_layernorm(x.data_ptr(), M, h, stride, g.data_ptr(),
+                                                    b.data_ptr(), y.data_ptr(), _stream(stream)))
+    return y
+
+
+def linear_ws_bytes(M, N, K):
+    return lib().flexq_linear_w4_workspace_size(M, N, K)
+
+
+def _ws(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def linear_w4(x, w: W4, bias=None, residual=None, relu=False, out=None, ws=None, stream=None):
+    _need(x, torch.float16, "x")
+    M = x.numel() // w.cols
+    y = out if out is not None else torch.empty(M, w.rows, dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = _ws(linear_ws_bytes(M, w.rows, w.cols), x.device)
+    wc = w.c()
+    _check("flexq_linear_w4", lib().flexq_linear_w4(
+        x.data_ptr(), M, C.byref(wc), _ptr(bias), _ptr(residual), int(relu), y.data_ptr(),
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def linear_w4_f32(x, w: W4, out=None, ws=None, stream=None):
+    _need(x, torch.float16, "x")
+    M = x.numel() // w.cols
+    y = out if out is not None else torch.empty(M, w.rows, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _ws(linear_ws_bytes(M, w.rows, w.cols), x.device)
+    wc = w.c()
+    _check("flexq_linear_w4_f32", lib().flexq_linear_w4_f32(
+        x.data_ptr(), M, C.byref(wc), y.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
+    return y
+
+
+def attn_prefill(qkv, B, S, kv: KV4, b0=0, out=None, stream=None):
+    _need(qkv, torch.float16, "qkv")
+    h = kv.heads * kv.head_dim
+    y = out if out is not None else torch.empty(B * S, h, dtype=torch.float16, device=qkv.device)
+    kc = kv.c()
+    _check("flexq_attn_prefill", lib().flexq_attn_prefill(qkv.data_ptr(), B, S, b0, C.byref(kc),
+                                                          y.data_ptr(), _stream(stream)))
+    return y
+
+
+def attn_decode_ws_bytes(B, heads, head_dim, pos):
+    return lib().flexq_attn_decode_workspace_size(B, heads, head_dim, pos)
+
+
+def attn_decode(qkv, pos, kv: KV4, b0=0, out=None, ws=None, stream=None):
+    _need(qkv, torch.float16, "qkv")
+    B = qkv.shape[0]
+    h = kv.heads * kv.head_dim
+    y = out if out is not None else torch.empty(B, h, dtype=torch.float16, device=qkv.device)
+    if ws is None:
+        ws = _ws(attn_decode_ws_bytes(B, kv.heads, kv.head_dim, pos), qkv.device)
+    kc = kv.c()
+    _check("flexq_attn_decode_kv4", lib().flexq_attn_decode_kv4(
+        qkv.data_ptr(), B, b0, pos, C.byref(kc), y.data_ptr(), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def embed(tokens, pos_base, seq, emb: W4, pos_table, out=None, stream=None):
+    _need(tokens, torch.int32, "tokens")
+    n = tokens.numel()
+    y = out if out is not None else torch.empty(n, emb.cols, dtype=torch.float16,
+                                                device=tokens.device)
+    ec = emb.c()
+    _check("flexq_embed", lib().flexq_embed(tokens.data_ptr(), n, pos_base, seq, C.byref(ec),
+                                            pos_table.data_ptr(), pos_table.shape[0],
+                                            y.data_ptr(), _stream(stream)))
+    return y
+
+
+def argmax(logits, out=None, stream=None):
+    M, N = logits.shape
+    y = out if out is not None else torch.empty(M, dtype=torch.int32, device=logits.device)
+    _check("flexq_argmax", lib().flexq_argmax(logits.data_ptr(), M, N, y.data_ptr(),
+                                              _stream(stream)))
+    return y
+
+
+# ------------------------------------------------------------------ layers and models
+
+class QLayer:
+    """fp16 vectors + four W4 matrices of one decoder layer, resident on the device."""
+
+    VECS = ("ln1_g", "ln1_b", "bqkv", "bo", "ln2_g", "ln2_b", "b1", "b2")
+    MATS = ("wqkv", "wo", "w1", "w2")
+
+    def __init__(self, vecs: dict, mats: dict, heads: int):
+        self.v = vecs
+        self.m = mats
+        self.heads = heads
+        self.hidden = mats["wo"].rows
+        self.ffn = mats["w1"].rows
+        self.head_dim = self.hidden // heads
+
+    @staticmethod
+    def from_fp16(w16: dict, heads: int, device="cuda", stream=None):
+        """Quantizes the four matrices with flexq_quantize; vectors stay fp16."""
+        vecs = {k: w16[k].to(device).contiguous() for k in QLayer.VECS}
+        mats = {k: quantize(w16[k].to(device).contiguous(), stream=stream) for k in QLayer.MATS}
+        return QLayer(vecs, mats, heads)
+
+    def c(self) -> LayerStruct:
+        v, m = self.v, self.m
+        return LayerStruct(v["ln1_g"].data_ptr(), v["ln1_b"].data_ptr(), m["wqkv"].c(),
+                           v["bqkv"].data_ptr(), m["wo"].c(), v["bo"].data_ptr(),
+                           v["ln2_g"].data_ptr(), v["ln2_b"].data_ptr(), m["w1"].c(),
+                           v["b1"].data_ptr(), m["w2"].c(), v["b2"].data_ptr())
+
+    def weight_bytes(self):
+        return sum(w.nbytes() for w in self.m.values())
+
+
+def layer_ws_bytes(hidden, heads, ffn, rows, max_len):
+    return lib().flexq_layer_workspace_size(hidden, heads, ffn, rows, max_len)
+
+
+def prefill_layer(layer: QLayer, kv: KV4, x, nb, S, b0=0, out=None, ws=None, stream=None):
+    _need(x, torch.float16, "x")
+    y = out if out is not None else torch.empty_like(x)
+    if ws is None:
+        ws = _ws(layer_ws_bytes(layer.hidden, layer.heads, layer.ffn, nb * S, 0), x.device)
+    lc, kc = layer.c(), kv.c()
+    _check("flexq_prefill_layer", lib().flexq_prefill_layer(
+        C.byref(lc), C.byref(kc), layer.hidden, layer.heads, layer.ffn, x.data_ptr(), nb, S, b0,
+        y.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def decode_layer(layer: QLayer, kv: KV4, x, pos, b0=0, out=None, ws=None, stream=None):
+    _need(x, torch.float16, "x")
+    B = x.shape[0]
+    y = out if out is not None else torch.empty_like(x)
+    if ws is None:
+        ws = _ws(layer_ws_bytes(layer.hidden, layer.heads, layer.ffn, B, pos + 1), x.device)
+    lc, kc = layer.c(), kv.c()
+    _check("flexq_decode_layer", lib().flexq_decode_layer(
+        C.byref(lc), C.byref(kc), layer.hidden, layer.heads, layer.ffn, x.data_ptr(), B, b0, pos,
+        y.data_ptr(), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+class QModel:
+    """An OPT-shaped model with 4-bit weights and per-layer 4-bit KV caches."""
+
+    def __init__(self, layers: list, embed_w4: W4, pos16, lnf_g, lnf_b, heads, batch, max_len,
+                 max_prefill_rows, device="cuda"):
+        self.layers = layers
+        self.embed = embed_w4
+        self.pos = pos16
+        self.lnf_g, self.lnf_b = lnf_g, lnf_b
+        self.heads = heads
+        self.hidden = embed_w4.cols
+        self.vocab = embed_w4.rows
+        self.ffn = layers[0].ffn
+        self.batch, self.max_len = batch, max_len
+        hd = self.hidden // heads
+        self.caches = [KV4(batch, heads, hd, max_len, device) for _ in layers]
+        nbytes = lib().flexq_model_workspace_size(self.hidden, heads, self.ffn, self.vocab,
+                                                  max_prefill_rows, batch, max_len)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._layer_arr = (LayerStruct * len(layers))(*[L.c() for L in layers])
+        self._kv_arr = (KV4Struct * len(layers))(*[k.c() for k in self.caches])
+        self._struct = ModelStruct(len(layers), self.hidden, heads, self.ffn, self.vocab,
+                                   pos16.shape[0], self._layer_arr, self._kv_arr, embed_w4.c(),
+                                   pos16.data_ptr(), lnf_g.data_ptr(), lnf_b.data_ptr(),
+                                   self.workspace.data_ptr(), nbytes)
+
+    def prefill(self, tokens, b0=0, logits=None, next_out=None, stream=None):
+        _need(tokens, torch.int32, "tokens")
+        nb, S = tokens.shape
+        nxt = next_out if next_out is not None else torch.empty(nb, dtype=torch.int32,
+                                                                device=tokens.device)
+        _check("flexq_prefill", lib().flexq_prefill(C.byref(self._struct), tokens.data_ptr(), nb,
+                                                    S, b0, nxt.data_ptr(), _ptr(logits),
+                                                    _stream(stream)))
+        return nxt
+
+    def decode_step(self, tokens, pos, logits=None, next_out=None, stream=None):
+        _need(tokens, torch.int32, "tokens")
+        B = tokens.numel()
+        nxt = next_out if next_out is not None else torch.empty(B, dtype=torch.int32,
+                                                                device=tokens.device)
+        _check("flexq_decode_step", lib().flexq_decode_step(C.byref(self._struct),
+                                                            tokens.data_ptr(), B, pos,
+                                                            nxt.data_ptr(), _ptr(logits),
+                                                            _stream(stream)))
+        return nxt
+
+    def weight_bytes(self):
+        return sum(L.weight_bytes() for L in self.layers) + self.embed.nbytes()

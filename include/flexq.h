@@ -1,0 +1,246 @@
+/*
+ * flexq — group-wise 4-bit weight + KV-cache OPT decoder path on MI355X (gfx950).
+ *
+ * C ABI of the HIP library libflexq.so.
+ *
+ * Conventions shared by every call
+ *   - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless the
+ *     comment says "host".  The library never allocates, frees or keeps device
+ *     memory; scratch space comes in through an explicit workspace argument whose
+ *     required size a *_workspace_size() call reports.
+ *   - Arrays are row-major, innermost dimension contiguous.
+ *   - Calls check their arguments on the host, then enqueue their kernels on
+ *     `stream` and return without waiting.  A rejected call enqueues nothing.
+ *     A launch failure reported by the runtime returns FLEXQ_ERR_DEVICE; a fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - No global state: calls on distinct streams and buffers may run concurrently.
+ *   - Results are deterministic: fixed reduction and merge orders.
+ *
+ * Compressed formats (FlexGen source walkthrough, section 6.3: num_bits 4,
+ * group_size 64, asymmetric; weights grouped along group_dim 0, the cache along
+ * group_dim 2; codes packed two per byte next to one fp16 parameter tensor)
+ *   - A group is 64 consecutive elements of the innermost dimension.
+ *   - codes:  uint8 [..][cols/2]; element 2j in the low nibble of byte j,
+ *             element 2j+1 in the high nibble.
+ *   - params: uint16 [..][cols/64][2] = (offset, scale) as fp16 per group; the
+ *             value of code c is c * scale + offset (scale = (max - min) / 15,
+ *             offset = min).  0.5625 bytes per element in total.
+ */
+#ifndef FLEXQ_H
+#define FLEXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLEXQ_OK = 0,
+  FLEXQ_ERR_INVALID = -1,     /* bad pointer, size, layout or workspace too small */
+  FLEXQ_ERR_UNSUPPORTED = -2, /* a valid configuration this build does not implement */
+  FLEXQ_ERR_DEVICE = -3       /* the HIP runtime reported an error at launch */
+} flexq_status;
+
+/* CompressionConfig of the pages (walkthrough section 6.3).  This build accepts
+ * {num_bits 4, group_size 64, symmetric 0} and returns FLEXQ_ERR_UNSUPPORTED for
+ * anything else. */
+typedef struct {
+  int32_t num_bits;
+  int32_t group_size;
+  int32_t symmetric;
+} flexq_qconfig;
+
+/* A 4-bit weight matrix W[rows][cols] (rows = N outputs, cols = K inputs),
+ * grouped along cols: codes [rows][cols/2], params [rows][cols/64][2]. */
+typedef struct {
+  const uint8_t* codes;
+  const uint16_t* params;
+  int64_t rows;
+  int64_t cols;
+} flexq_w4;
+
+/* The 4-bit KV cache of one layer.  Groups are 64 consecutive head_dim elements
+ * of one token's K (or V) vector in one head.
+ *   k_codes, v_codes   [batch][heads][max_len][head_dim/2]
+ *   k_params, v_params [batch][heads][max_len][head_dim/64][2]      */
+typedef struct {
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_params;
+  uint16_t* v_params;
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim; /* 64 or 128 */
+  int32_t max_len;
+} flexq_kv4_layer;
+
+/* Weights of one pre-LayerNorm OPT decoder layer (source notes, "Flex Opt": the
+ * model is an embedding, N transformer layers and an output head).  fp16 vectors
+ * of length hidden (LN gains/biases, bo, b2), 3*hidden (bqkv) or ffn (b1).
+ * wqkv [3h][h] produces [Q | K | V], each head-major (head * head_dim + d). */
+typedef struct {
+  const uint16_t *ln1_g, *ln1_b;
+  flexq_w4 wqkv;
+  const uint16_t* bqkv;
+  flexq_w4 wo;
+  const uint16_t* bo;
+  const uint16_t *ln2_g, *ln2_b;
+  flexq_w4 w1;
+  const uint16_t* b1;
+  flexq_w4 w2;
+  const uint16_t* b2;
+} flexq_layer;
+
+/* Optional launch timing: when a model carries a trace, flexq_prefill and
+ * flexq_decode_step record events[2i] / events[2i+1] on their stream right before
+ * and after each 4-bit linear layer they launch (split-K reduction included) and
+ * note which one in kinds[i] (FLEXQ_TRACE_*) and its row count in rows[i].  The
+ * caller creates the 2*capacity events (HOST array) and resets count; recording
+ * stops silently when count reaches capacity. */
+enum { FLEXQ_TRACE_QKV = 0, FLEXQ_TRACE_OUT = 1, FLEXQ_TRACE_FC1 = 2, FLEXQ_TRACE_FC2 = 3,
+       FLEXQ_TRACE_HEAD = 4 };
+typedef struct {
+  hipEvent_t* events;
+  int32_t* kinds;
+  int64_t* rows;
+  int32_t capacity;
+  int32_t count;
+} flexq_trace;
+
+/* A whole OPT-shaped model.  Non-owning: every pointer stays the caller's.
+ * `layer` and `kv` are HOST arrays of `layers` entries (the structs inside hold
+ * device pointers).  embed is the 4-bit token embedding [vocab][hidden], also used
+ * as the LM head (tied, no bias).  pos is the fp16 learned-position table
+ * [pos_rows][hidden]; position p reads row p + 2.  workspace must hold
+ * flexq_model_workspace_size(...) bytes. */
+typedef struct {
+  int32_t layers, hidden, heads, ffn, vocab, pos_rows;
+  const flexq_layer* layer;
+  const flexq_kv4_layer* kv;
+  flexq_w4 embed;
+  const uint16_t* pos;
+  const uint16_t *lnf_g, *lnf_b;
+  void* workspace;
+  size_t workspace_bytes;
+  flexq_trace* trace; /* NULL, or a HOST trace (see flexq_trace) */
+} flexq_model;
+
+const char* flexq_status_string(int status);
+
+/* ---------------------------------------------------------------- quantize/pack
+ * Group-wise min/max asymmetric 4-bit quantization (walkthrough section 6.3,
+ * `compress`).  x fp16 [rows][cols], cols a multiple of 64, values finite.
+ * Writes codes [rows][cols/2] and params [rows][cols/64][2].  Per group, in fp32:
+ * step = fp16(fl32(max - min) / 15) (0 for a constant group, 2^-24 if the step
+ * underflows), code = clamp(rne(fl32(x - min) * fl32(1 / step)), 0, 15), offset =
+ * min with a zero stored as +0.  Bit-identical to the oracle on identical input. */
+int flexq_quantize(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
+                   uint8_t* codes, uint16_t* params, hipStream_t stream);
+
+/* Inverse of flexq_quantize for weights (`decompress`): out fp16 [rows][cols] =
+ * fp16(code * scale + offset) with one rounding.  A test and inspection aid; the
+ * GEMMs dequantize inside their own tiles. */
+int flexq_dequantize(const uint8_t* codes, const uint16_t* params, int64_t rows, int64_t cols,
+                     uint16_t* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- LayerNorm
+ * y[m] = (x[m] - mean) / sqrt(biased var + 1e-5) * g + b, statistics in fp32,
+ * fp16 out.  Row m of x starts at x + m * x_row_stride (elements); y is dense
+ * [M][h].  h a multiple of 8. */
+int flexq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64_t x_row_stride,
+                    const uint16_t* g, const uint16_t* b, uint16_t* y, hipStream_t stream);
+
+/* ---------------------------------------------------------------- 4-bit linear
+ * y[M][N] = fp16( [relu](x . W^T + bias) [+ residual] ), W = fp16-dequantized
+ * 4-bit weight [N][K] (the pages' fp16 linear layers with compressed weights).
+ * x fp16 [M][K]; bias fp16 [N] or NULL; residual fp16 [M][N] or NULL (may equal
+ * y); relu 0/1.  fp16 MFMA operands, fp32 accumulation, one rounding at the end.
+ * K a multiple of 64.  ws: scratch for split-K partial sums, at least
+ * flexq_linear_w4_workspace_size(M, N, K) bytes (may be 0 -> NULL allowed). */
+size_t flexq_linear_w4_workspace_size(int64_t M, int64_t N, int64_t K);
+int flexq_linear_w4(const uint16_t* x, int64_t M, const flexq_w4* W, const uint16_t* bias,
+                    const uint16_t* residual, int32_t relu, uint16_t* y, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Same product written as fp32 without bias, activation or rounding: y32 [M][N].
+ * Used for logits against the tied embedding (`opt_output_embed`). */
+int flexq_linear_w4_f32(const uint16_t* x, int64_t M, const flexq_w4* W, float* y32,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- attention
+ * Prefill attention (source notes, "Pytorch Backend": `mha`).  qkv fp16
+ * [B*S][3h], rows ordered (b, t).  For each sequence and head: causal
+ * softmax(q k^T / sqrt(head_dim)) v over the fp16 K/V of this pass (fp32 scores
+ * and softmax), output fp16 out [B*S][h].  K and V of the S positions are then
+ * quantized into cache rows b0 .. b0+B-1, positions [0, S).  Needs
+ * b0 + B <= kv->batch and S <= kv->max_len. */
+int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int32_t b0,
+                       const flexq_kv4_layer* kv, uint16_t* out, hipStream_t stream);
+
+/* Decode attention over the 4-bit cache (`mha_gen`).  qkv fp16 [B][3h], one new
+ * token per sequence for cache rows b0 .. b0+B-1.  The token's k, v are quantized
+ * into position pos, then positions [0, pos] are read back from the cache (codes
+ * dequantized to fp32), softmax in fp32, output fp16 out [B][h].  The context is
+ * split over work-groups (split-K) and merged with an online-softmax rescale in a
+ * fixed order.  ws: at least flexq_attn_decode_workspace_size(...) bytes. */
+size_t flexq_attn_decode_workspace_size(int32_t B, int32_t heads, int32_t head_dim, int32_t pos);
+int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                          const flexq_kv4_layer* kv, uint16_t* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ---------------------------------------------------------------- model pieces
+ * Token + position embedding (`opt_input_embed`, source notes "Pytorch Backend"):
+ * out[m] = fp16(dequant(embed row tokens[m]) + pos[p + 2]) with position
+ * p = pos_base + m % seq (prefill: pos_base 0, seq S; decode: pos_base = pos,
+ * seq 1).  tokens: device int32 [n], ids outside [0, vocab) are clamped.
+ * pos_base + min(n, seq) - 1 + 2 must be < pos_rows. */
+int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, int32_t seq,
+                const flexq_w4* embed, const uint16_t* pos, int32_t pos_rows, uint16_t* out,
+                hipStream_t stream);
+
+/* Greedy pick: next[m] = argmax_n logits[m][n], lowest index among equal maxima. */
+int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next, hipStream_t stream);
+
+/* One decoder layer, prefill of nb sequences of S tokens: x_out [nb*S][h] from
+ * x_in [nb*S][h] (distinct buffers), filling cache rows b0.. positions [0, S). */
+size_t flexq_layer_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, int64_t rows,
+                                  int32_t max_len);
+int flexq_prefill_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t hidden,
+                        int32_t heads, int32_t ffn, const uint16_t* x_in, int32_t nb, int32_t S,
+                        int32_t b0, uint16_t* x_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+/* One decoder layer, one decode step of B sequences at position pos. */
+int flexq_decode_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t hidden,
+                       int32_t heads, int32_t ffn, const uint16_t* x_in, int32_t B, int32_t b0,
+                       int32_t pos, uint16_t* x_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------- whole model
+ * Workspace for prefill micro-batches of up to max_prefill_rows = nb*S token
+ * rows and decode batches of up to max_batch sequences with caches of max_len. */
+size_t flexq_model_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, int32_t vocab,
+                                  int64_t max_prefill_rows, int32_t max_batch, int32_t max_len);
+
+/* Prefill of one micro-batch (source notes, "Flex Opt": embedding, layers, output
+ * head): tokens int32 [nb][S] for cache rows b0..b0+nb-1.  Writes the first
+ * generated token of each sequence to next [nb] and, if logits != NULL, the fp32
+ * logits of the last prompt position to logits [nb][vocab]. */
+int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32_t S, int32_t b0,
+                  int32_t* next, float* logits, hipStream_t stream);
+
+/* One greedy decode step of B sequences (cache rows 0..B-1): tokens int32 [B]
+ * at position pos -> next [B] (and logits [B][vocab] if not NULL).  The call
+ * neither synchronises nor allocates, so a caller may capture it in a HIP graph
+ * (pos is baked into the captured kernels). */
+int flexq_decode_step(const flexq_model* m, const int32_t* tokens, int32_t B, int32_t pos,
+                      int32_t* next, float* logits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLEXQ_H */
