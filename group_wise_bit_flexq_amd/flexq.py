@@ -223,6 +223,7 @@ def linear_w4(x, w: W4, bias=None, residual=None, relu=False, out=None, ws=None,
     _need(x, torch.float16, "x")
     M = x.numel() // w.cols
     y = out if out is not None else torch.empty(M, w.rows, dtype=torch.float16, device=x.device)
+    _need(y, torch.float16, "out")
     if ws is None:
         ws = _ws(linear_ws_bytes(M, w.rows, w.cols), x.device)
     wc = w.c()
@@ -236,6 +237,7 @@ def linear_w4_f32(x, w: W4, out=None, ws=None, stream=None):
     _need(x, torch.float16, "x")
     M = x.numel() // w.cols
     y = out if out is not None else torch.empty(M, w.rows, dtype=torch.float32, device=x.device)
+    _need(y, torch.float32, "out")
     if ws is None:
         ws = _ws(linear_ws_bytes(M, w.rows, w.cols), x.device)
     wc = w.c()
@@ -387,6 +389,9 @@ class QModel:
         nb, S = tokens.shape
         nxt = next_out if next_out is not None else torch.empty(nb, dtype=torch.int32,
                                                                 device=tokens.device)
+        _need(nxt, torch.int32, "next_out")
+        if logits is not None:
+            _need(logits, torch.float32, "logits")
         _check("flexq_prefill", lib().flexq_prefill(C.byref(self._struct), tokens.data_ptr(), nb,
                                                     S, b0, nxt.data_ptr(), _ptr(logits),
                                                     _stream(stream)))
@@ -397,6 +402,9 @@ class QModel:
         B = tokens.numel()
         nxt = next_out if next_out is not None else torch.empty(B, dtype=torch.int32,
                                                                 device=tokens.device)
+        _need(nxt, torch.int32, "next_out")
+        if logits is not None:
+            _need(logits, torch.float32, "logits")
         _check("flexq_decode_step", lib().flexq_decode_step(C.byref(self._struct),
                                                             tokens.data_ptr(), B, pos,
                                                             nxt.data_ptr(), _ptr(logits),

@@ -149,9 +149,14 @@ def linear_w4(x, codes, params, bias=None, residual=None, relu=False, out_dtype=
 
     One rounding to `out_dtype` at the end (fp16 for hidden states, float64 for logits).
     """
+    return linear_dequantized(x, dequantize_weight(codes, params).astype(F64), bias, residual,
+                              relu, out_dtype)
+
+
+def linear_dequantized(x, w64, bias=None, residual=None, relu=False, out_dtype=F16):
+    """`linear_w4` with the weight already dequantized (float64 copy of its fp16 values)."""
     x = np.asarray(x, dtype=F16).astype(F64)
-    w = dequantize_weight(codes, params).astype(F64)
-    return _finish_linear(x @ w.T, bias, residual, relu, out_dtype)
+    return _finish_linear(x @ w64.T, bias, residual, relu, out_dtype)
 
 
 def linear_w4_sampled(x, codes, params, rows, cols, bias=None, residual=None, relu=False):
@@ -280,17 +285,19 @@ class QLayer:
         self.head_dim = self.hidden // heads
         self.p = {k: np.asarray(v, dtype=F16) for k, v in w16.items() if not k.startswith("w")}
         self.q = {k: quantize(np.asarray(w16[k], dtype=F16)) for k in ("wqkv", "wo", "w1", "w2")}
+        # weights are decompressed once (to fp16, held as float64), not on every call
+        self.w = {k: dequantize_weight(*self.q[k]).astype(F64) for k in self.q}
 
     def _attn_block(self, x, attn_fn):
         a = layernorm(x, self.p["ln1_g"], self.p["ln1_b"])
-        qkv = linear_w4(a, *self.q["wqkv"], bias=self.p["bqkv"])
+        qkv = linear_dequantized(a, self.w["wqkv"], bias=self.p["bqkv"])
         o = attn_fn(qkv)
-        return linear_w4(o, *self.q["wo"], bias=self.p["bo"], residual=x)
+        return linear_dequantized(o, self.w["wo"], bias=self.p["bo"], residual=x)
 
     def _mlp_block(self, x1):
         a = layernorm(x1, self.p["ln2_g"], self.p["ln2_b"])
-        u = linear_w4(a, *self.q["w1"], bias=self.p["b1"], relu=True)
-        return linear_w4(u, *self.q["w2"], bias=self.p["b2"], residual=x1)
+        u = linear_dequantized(a, self.w["w1"], bias=self.p["b1"], relu=True)
+        return linear_dequantized(u, self.w["w2"], bias=self.p["b2"], residual=x1)
 
     def prefill(self, x, batch, seq, cache, b0=0):
         """x fp16 [batch*seq][h] -> fp16 [batch*seq][h]; fills cache positions [0, seq)."""
@@ -313,14 +320,16 @@ def embed(tokens, positions, e_codes, e_params, pos_table, pos_offset=2):
     return (tok + pos).astype(F16)
 
 
-def lm_head(x_last, lnf_g, lnf_b, e_codes, e_params):
+def lm_head(x_last, lnf_g, lnf_b, e_codes, e_params, e_w64=None):
     """Final LayerNorm, logits against the tied 4-bit embedding (no bias), greedy pick.
 
     Returns (logits float64 [nb][V], next token int32 [nb]); np.argmax takes the lowest
-    index among equal maxima.
+    index among equal maxima.  e_w64: the embedding already dequantized, if at hand.
     """
     a = layernorm(x_last, lnf_g, lnf_b)
-    logits = linear_w4(a, e_codes, e_params, out_dtype=F64)
+    if e_w64 is None:
+        e_w64 = dequantize_weight(e_codes, e_params).astype(F64)
+    logits = linear_dequantized(a, e_w64, out_dtype=F64)
     return logits, np.argmax(logits, axis=-1).astype(np.int32)
 
 
@@ -331,6 +340,7 @@ class QModel:
         self.layers = layers
         self.heads = heads
         self.e_codes, self.e_params = quantize(np.asarray(embed16, dtype=F16))
+        self.e_w = dequantize_weight(self.e_codes, self.e_params).astype(F64)
         self.pos = np.asarray(pos16, dtype=F16)
         self.lnf_g = np.asarray(lnf_g, dtype=F16)
         self.lnf_b = np.asarray(lnf_b, dtype=F16)
@@ -347,7 +357,7 @@ class QModel:
         for L, c in zip(self.layers, caches):
             x = L.prefill(x, nb, seq, c, b0)
         last = x.reshape(nb, seq, -1)[:, -1]
-        return lm_head(last, self.lnf_g, self.lnf_b, self.e_codes, self.e_params)
+        return lm_head(last, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
     def decode_step(self, tokens, pos, caches, b0=0):
         """tokens int [nb] at position pos -> (logits [nb][V], next token [nb])."""
@@ -355,7 +365,7 @@ class QModel:
         x = embed(tokens, np.full(tokens.shape, pos), self.e_codes, self.e_params, self.pos)
         for L, c in zip(self.layers, caches):
             x = L.decode(x, pos, c, b0)
-        return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params)
+        return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
     def generate(self, tokens, gen):
         """Greedy generation of `gen` tokens ([WALK] section 4.1, do_sample=False)."""

@@ -1,0 +1,138 @@
+"""Full-size parity on sampled outputs: one OPT-30B- and one OPT-175B-shaped layer.
+
+The layer runs at its real shapes in the launch configuration the benchmark uses:
+prefill of three micro-batches of 48 x 512 tokens (M = 24576 per GEMM) into a 4-bit
+cache for 144 sequences, then one decode step of the whole batch (M = 144) at
+position 512.  The oracle cannot afford whole outputs here, so it recomputes sampled
+elements one by one from the GPU's inputs to each op (teacher-forced): GEMM entries,
+LayerNorm rows, attention rows of sampled (sequence, head) pairs, and the 4-bit codes
+of sampled weight rows and cache rows, which must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from group_wise_bit_flexq_amd import synth
+from group_wise_bit_flexq_amd.workloads import WORKLOADS
+from oracle import flexq_oracle as O
+from tests.gpu_helpers import F16, assert_close_fp16, require_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _check_linear(x_gpu, w16_gpu, wq, y_gpu, rng, what, bias=None, res=None, relu=False, n=48):
+    """Sampled (m, n) entries of y against the oracle, weights re-quantized by the oracle."""
+    M, K = x_gpu.shape
+    N = w16_gpu.shape[0]
+    ms = rng.integers(0, M, n)
+    ns = rng.integers(0, N, n)
+    wrows = to_np(w16_gpu[torch.from_numpy(ns).cuda()])
+    codes, params = O.quantize(wrows)
+    assert np.array_equal(codes, to_np(wq.codes[torch.from_numpy(ns).cuda()])), what + " codes"
+    xs = to_np(x_gpu[torch.from_numpy(ms).cuda()])
+    b = None if bias is None else to_np(bias)[ns]
+    r = None if res is None else to_np(res[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])
+    # sample i is entry (i, i) of the oracle's product of the sampled rows
+    R = None
+    if r is not None:
+        R = np.zeros((n, n), F16)
+        R[np.arange(n), np.arange(n)] = r
+    ref = O.linear_w4_sampled(xs, codes, params, np.arange(n), np.arange(n), bias=b, residual=R,
+                              relu=relu)
+    got = to_np(y_gpu[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])
+    wd = O.dequantize_weight(codes, params).astype(np.float64)
+    bound = K * 2.0**-24 * np.sum(np.abs(xs.astype(np.float64)) * np.abs(wd), axis=1)
+    assert_close_fp16(got, ref, extra=bound, what=what)
+
+
+def _head_qkv(qkv_rows, head, hd, h):
+    q = qkv_rows[:, head * hd:(head + 1) * hd]
+    k = qkv_rows[:, h + head * hd:h + (head + 1) * hd]
+    v = qkv_rows[:, 2 * h + head * hd:2 * h + (head + 1) * hd]
+    return np.concatenate([q, k, v], axis=1)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["opt30b", "opt175b"])
+def test_fullsize_layer_sampled(name):
+    F = require_gpu()
+    wl = WORKLOADS[name]
+    h, nh, hd, f, B, mb, S = wl.hidden, wl.heads, wl.head_dim, wl.ffn, wl.batch, wl.micro_batch, wl.prompt
+    _say("full-size layer", name, h, nh, f, B, mb, S)
+    rng = np.random.default_rng({"opt30b": 30, "opt175b": 175}[name])
+    layer = wl.layers - 1
+    w16 = synth.layer_weights_fp16(h, f, 0, layer, device="cuda")
+    L = F.QLayer.from_fp16(w16, nh)
+    v = L.v
+    kv = F.KV4(B, nh, hd, S + 1)
+    check_mb = 1
+    kept = None
+    for j in range(B // mb):
+        x = synth.normal_fp16((mb * S, h), 1.0, synth.sub_seed(0, "x", j), device="cuda")
+        a = F.layernorm(x, v["ln1_g"], v["ln1_b"])
+        qkv = F.linear_w4(a, L.m["wqkv"], bias=v["bqkv"])
+        att = F.attn_prefill(qkv, mb, S, kv, b0=j * mb)
+        x1 = F.linear_w4(att, L.m["wo"], bias=v["bo"], residual=x)
+        a2 = F.layernorm(x1, v["ln2_g"], v["ln2_b"])
+        u = F.linear_w4(a2, L.m["w1"], bias=v["b1"], relu=True)
+        y = F.linear_w4(u, L.m["w2"], bias=v["b2"], residual=x1)
+        torch.cuda.synchronize()
+        if j != check_mb:
+            continue
+        _say("prefill checks", name)
+        rows = rng.integers(0, mb * S, 4)
+        ln_ref = O.layernorm(to_np(x[torch.from_numpy(rows).cuda()]), to_np(v["ln1_g"]),
+                             to_np(v["ln1_b"]))
+        assert_close_fp16(to_np(a[torch.from_numpy(rows).cuda()]), ln_ref, extra=1e-4, what="ln1")
+        _check_linear(a, w16["wqkv"], L.m["wqkv"], qkv, rng, "qkv", bias=v["bqkv"])
+        _check_linear(att, w16["wo"], L.m["wo"], x1, rng, "out", bias=v["bo"], res=x)
+        _check_linear(a2, w16["w1"], L.m["w1"], u, rng, "fc1", bias=v["b1"], relu=True)
+        _check_linear(u, w16["w2"], L.m["w2"], y, rng, "fc2", bias=v["b2"], res=x1)
+        # attention rows and cache codes of sampled (sequence, head) pairs
+        kept = {}
+        for _ in range(3):
+            b = int(rng.integers(0, mb))
+            hh = int(rng.integers(0, nh))
+            qrows = to_np(qkv[b * S:(b + 1) * S])
+            small = _head_qkv(qrows, hh, hd, h)
+            oc = O.KVCache(1, 1, hd, S + 1)
+            ref = O.attn_prefill(small, 1, S, 1, hd, oc)
+            got = to_np(att[b * S:(b + 1) * S, hh * hd:(hh + 1) * hd])
+            assert_close_fp16(got, ref, extra=2.0**-9 * np.abs(small.astype(np.float64)).max(),
+                              what=f"prefill attention b={b} head={hh}")
+            bb = j * mb + b
+            assert np.array_equal(to_np(kv.k_codes[bb, hh, :S]), oc.k_codes[0, 0, :S])
+            assert np.array_equal(to_np(kv.v_codes[bb, hh, :S]), oc.v_codes[0, 0, :S])
+            assert np.array_equal(to_np(kv.k_params[bb, hh, :S]).view(np.uint16),
+                                  oc.k_params[0, 0, :S].view(np.uint16))
+            kept[(bb, hh)] = oc
+        del qkv, att, x1, a2, u, y, a, x
+
+    _say("decode step", name)
+    xd = synth.normal_fp16((B, h), 1.0, synth.sub_seed(0, "xd", 0), device="cuda")
+    a = F.layernorm(xd, v["ln1_g"], v["ln1_b"])
+    qkv = F.linear_w4(a, L.m["wqkv"], bias=v["bqkv"])
+    att = F.attn_decode(qkv, S, kv)
+    x1 = F.linear_w4(att, L.m["wo"], bias=v["bo"], residual=xd)
+    a2 = F.layernorm(x1, v["ln2_g"], v["ln2_b"])
+    u = F.linear_w4(a2, L.m["w1"], bias=v["b1"], relu=True)
+    y = F.linear_w4(u, L.m["w2"], bias=v["b2"], residual=x1)
+    torch.cuda.synchronize()
+    _check_linear(a, w16["wqkv"], L.m["wqkv"], qkv, rng, "decode qkv", bias=v["bqkv"])
+    _check_linear(att, w16["wo"], L.m["wo"], x1, rng, "decode out", bias=v["bo"], res=xd)
+    _check_linear(a2, w16["w1"], L.m["w1"], u, rng, "decode fc1", bias=v["b1"], relu=True)
+    _check_linear(u, w16["w2"], L.m["w2"], y, rng, "decode fc2", bias=v["b2"], res=x1)
+    qn = to_np(qkv)
+    for (bb, hh), oc in kept.items():
+        small = _head_qkv(qn[bb:bb + 1], hh, hd, h)
+        ref = O.attn_decode(small, S, oc)
+        got = to_np(att[bb:bb + 1, hh * hd:(hh + 1) * hd])
+        vmax = 15 * np.abs(oc.v_params[..., 1].astype(np.float64)).max() + \
+            np.abs(oc.v_params[..., 0].astype(np.float64)).max()
+        assert_close_fp16(got, ref, extra=2.0**-16 * vmax, what=f"decode attention b={bb} h={hh}")
+        assert np.array_equal(to_np(kv.k_codes[bb, hh, S]), oc.k_codes[0, 0, S])
+        assert np.array_equal(to_np(kv.v_codes[bb, hh, S]), oc.v_codes[0, 0, S])
