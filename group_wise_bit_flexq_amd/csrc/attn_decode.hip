@@ -79,8 +79,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
         if (sub == 0) pb[(slot0 + pos) * GPT + grp] = prm;
       }
     }
-    __threadfence();
   }
+  // only this work-group reads position pos in this launch: the barrier's
+  // work-group-scope release/acquire orders the append before the reads below
   __syncthreads();
 
   // ---- this lane's slice of q: dims 32 j .. 32 j + 31 (group j / 2)

@@ -35,10 +35,9 @@ struct GemmShape {
   static constexpr int THREADS = WM * WN * 64;
   static constexpr int A_CHUNKS = BM * 8;      // 16-B pieces of an A tile
   static constexpr int B_PIECES = BN * 2;      // 16-B code pieces (32 codes) of a B tile
-  static constexpr int A_PER_T = A_CHUNKS / THREADS;
+  static constexpr int A_PER_T = (A_CHUNKS + THREADS - 1) / THREADS;
   static constexpr int B_PER_T = (B_PIECES + THREADS - 1) / THREADS;
   static constexpr size_t LDS_BYTES = 2 * (size_t)(BM + BN) * kBK * sizeof(f16);
-  static_assert(A_CHUNKS % THREADS == 0, "A tile must split evenly over threads");
 };
 
 struct Epilogue {
@@ -85,8 +84,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
       const int idx = tid + j * S::THREADS;
       const int row = idx >> 3, ch = idx & 7;
       const int gm = m0 + row;
-      ra[j] = gm < M ? *(const uint4*)(X + (int64_t)gm * K + kt * kBK + ch * 8)
-                     : make_uint4(0, 0, 0, 0);
+      ra[j] = (idx < S::A_CHUNKS && gm < M)
+                  ? *(const uint4*)(X + (int64_t)gm * K + kt * kBK + ch * 8)
+                  : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < S::B_PER_T; ++j) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
 #pragma unroll
     for (int j = 0; j < S::A_PER_T; ++j) {
       const int idx = tid + j * S::THREADS;
-      *(uint4*)(a + lds_off(idx >> 3, idx & 7)) = ra[j];
+      if (idx < S::A_CHUNKS) *(uint4*)(a + lds_off(idx >> 3, idx & 7)) = ra[j];
     }
 #pragma unroll
     for (int j = 0; j < S::B_PER_T; ++j) {
@@ -233,7 +233,7 @@ struct Plan {
   int kt_per_split;
 };
 
-constexpr int kCfgPrefill = 0;  // 128 x 128, 2x2 waves of 64x64
+constexpr int kCfgPrefill = 0;  // 256 x 256, 2x4 waves of 128x64 (8 waves, 2 per SIMD)
 constexpr int kCfgM32 = 1;      // 32 x 128
 constexpr int kCfgM64 = 2;      // 64 x 128
 constexpr int kCfgM160 = 3;     // 160 x 128
@@ -243,7 +243,7 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   if (M <= 32) { p.cfg = kCfgM32; p.bm = 32; p.bn = 128; }
   else if (M <= 64) { p.cfg = kCfgM64; p.bm = 64; p.bn = 128; }
   else if (M <= 160) { p.cfg = kCfgM160; p.bm = 160; p.bn = 128; }
-  else { p.cfg = kCfgPrefill; p.bm = 128; p.bn = 128; }
+  else { p.cfg = kCfgPrefill; p.bm = 256; p.bn = 256; }
   const int64_t KT = K / kBK;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int splits = 1;
@@ -286,7 +286,7 @@ static void launch_plan(const Plan& p, const f16* x, const flexq_w4* W, int M, E
     case kCfgM32: launch_cfg<1, 4, 1, 1, OUT>(p, x, W, M, ep, Y, stream); break;
     case kCfgM64: launch_cfg<1, 4, 2, 1, OUT>(p, x, W, M, ep, Y, stream); break;
     case kCfgM160: launch_cfg<1, 4, 5, 1, OUT>(p, x, W, M, ep, Y, stream); break;
-    default: launch_cfg<2, 2, 2, 2, OUT>(p, x, W, M, ep, Y, stream); break;
+    default: launch_cfg<2, 4, 4, 2, OUT>(p, x, W, M, ep, Y, stream); break;
   }
 }
 

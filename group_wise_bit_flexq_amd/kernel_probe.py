@@ -1,0 +1,107 @@
+"""Kernel probes at workload shapes, for rocprofv3 kernel traces and counter runs.
+
+    python -m group_wise_bit_flexq_amd.kernel_probe gemm --workload opt175b --reps 2
+        the four prefill 4-bit GEMMs of one decoder layer (M = micro-batch x prompt
+        rows), launched exactly as the model path launches them;
+    python -m group_wise_bit_flexq_amd.kernel_probe decode --workload opt175b --reps 2
+        one decode step's 4-bit GEMMs (M = batch) and decode attention over a cache
+        of prompt + gen/2 positions;
+    python -m group_wise_bit_flexq_amd.kernel_probe copy --mib 1024 --reps 3
+        an elementwise device copy of a known size, the reference that scales the
+        HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above.
+Each prints its per-launch times (HIP events) as one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+
+def _time(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sum(ts) / len(ts)
+
+
+def gemm(wl, reps, rows):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    h, f = wl.hidden, wl.ffn
+    w16 = synth.layer_weights_fp16(h, f, 0, 0, device="cuda")
+    L = F.QLayer.from_fp16(w16, wl.heads)
+    del w16
+    res = {}
+    for name, (n, k) in {"wqkv": (3 * h, h), "wo": (h, h), "w1": (f, h), "w2": (h, f)}.items():
+        x = synth.normal_fp16((rows, k), 1.0, 1, device="cuda")
+        y = torch.empty(rows, n, dtype=torch.float16, device="cuda")
+        ws = torch.empty(max(F.linear_ws_bytes(rows, n, k), 16), dtype=torch.uint8, device="cuda")
+        ms = _time(lambda: F.linear_w4(x, L.m[name], bias=L.v["b1"] if name == "w1" else None,
+                                       out=y, ws=ws), reps)
+        res[name] = {"M": rows, "N": n, "K": k, "ms": ms, "tflops": 2 * rows * n * k / ms / 1e9}
+        del x, y, ws
+    return res
+
+
+def decode(wl, reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    res = gemm(wl, reps, wl.batch)
+    T = wl.prompt + wl.gen // 2
+    kv = F.KV4(wl.batch, wl.heads, wl.head_dim, T + 1)
+    qkv = torch.randn(wl.batch, 3 * wl.hidden, device="cuda").half()
+    out = torch.empty(wl.batch, wl.hidden, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(F.attn_decode_ws_bytes(wl.batch, wl.heads, wl.head_dim, T), 16),
+                     dtype=torch.uint8, device="cuda")
+    ms = _time(lambda: F.attn_decode(qkv, T, kv, out=out, ws=ws), reps)
+    nbytes = wl.batch * wl.heads * (T + 1) * 2 * wl.head_dim * 0.5625
+    res["attn_decode"] = {"T": T + 1, "ms": ms, "gbps": nbytes / ms / 1e6}
+    return res
+
+
+def copy(mib, reps):
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda").half()
+    dst = torch.empty_like(src)
+    ms = _time(lambda: torch.mul(src, 1.0, out=dst), reps)
+    return {"bytes_read": 2 * n, "bytes_written": 2 * n, "ms": ms, "gbps": 4 * n / ms / 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("what", choices=["gemm", "decode", "copy"])
+    ap.add_argument("--workload", default="opt175b")
+    ap.add_argument("--reps", type=int, default=2)
+    ap.add_argument("--mib", type=int, default=1024)
+    a = ap.parse_args()
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd.workloads import WORKLOADS
+    F.lib()
+    wl = WORKLOADS[a.workload]
+    if a.what == "gemm":
+        r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
+    elif a.what == "decode":
+        r = decode(wl, a.reps)
+    else:
+        r = copy(a.mib, a.reps)
+    print(json.dumps({"probe": a.what, "workload": a.workload, "results": r}), flush=True)
+
+
+if __name__ == "__main__":
+    main()
