@@ -317,7 +317,7 @@ def main():
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {
-            "kernel": "gemm_w4_kernel<2,4,4,2,0> (prefill, 256x256 tile, 8 waves)",
+            "kernel": "gemm_w4_big_kernel<2,4,4,2,0> (prefill, 256x256x64 tile, 8 waves)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_FP16_TFLOPS,

@@ -2,28 +2,32 @@
 //
 // The pages' linear layers are fp16 matmuls whose weights are stored compressed
 // (FlexGen walkthrough, section 6.3: weights grouped along the input dimension,
-// 64 per group, 4 bits, fp16 parameters).  Here the weight tile is expanded to fp16
-// on its way into LDS, once per work-group and k-step, and reused by every row of
-// the work-group's M tile:
+// 64 per group, 4 bits, fp16 parameters).  Two kernels share the arithmetic:
 //
-//   x  fp16 [M][K]         --global-->  LDS A tile  [BM][64]
-//   W  codes [N][K/2] + (offset, scale) per 64  --dequant (v_pk_fma_f16)-->  LDS B tile [BN][64]
-//   v_mfma_f32_32x32x16_f16  (fp16 operands, fp32 accumulators)
+//  * large M (prefill, M = 48 x 512): 256 x 256 x 64 tiles, 8 waves.  The weight
+//    tile is expanded to fp16 on its way into LDS (v_pk_fma_f16: one rounding of
+//    c * scale + offset), once per work-group and k-step, and reused by all 256 rows;
+//  * small M (decode, M = batch <= 160): weights are streamed once, straight into
+//    the registers of the wave that uses them, and dequantized there; only the
+//    activation tile goes through LDS.
 //
-// LDS rows are 128 B (one 64-element quantization group); 16-B chunk c of row r
-// lives at chunk c ^ (r & 7) so that 32 lanes reading 32 rows at one k offset hit
-// distinct banks.  Two LDS stages: the next tile's global loads are in flight while
-// the current tile feeds the MFMAs.  Work-groups are 256 threads (4 waves); the
-// wave grid WM x WN and per-wave 32x32 tile counts TM x TN set the block tile.
-// Split-K writes fp32 partial sums that a second kernel adds in split order.
+// Both feed v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulators) and finish
+// with a fused bias / ReLU / residual epilogue and a single fp16 rounding.  Where a
+// shape has too few tiles for 256 CUs, K is split and a second kernel adds the fp32
+// partial sums in split order (deterministic).
 #include "common.h"
 
 namespace flexq {
 
 constexpr int kBK = 64;
 
+// LDS tile rows are 128 B (8 chunks of 16 B).  gfx950's LDS serves 16 lanes of a
+// 128-bit access per cycle from 64 banks, i.e. 16 slots of 16 B, and slot =
+// 8 * (row & 1) + chunk for an unswizzled tile; storing chunk c of row r at chunk
+// c ^ ((r >> 1) & 7) gives 16 consecutive rows read at one k offset 16 distinct
+// slots, and keeps the row-wise stores conflict-free as well.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);  // in fp16 elements
+  return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3);  // in fp16 elements
 }
 
 enum OutKind { kOutF16 = 0, kOutF32 = 1, kOutPartial = 2 };
@@ -54,85 +58,143 @@ __device__ __forceinline__ float epilogue_value(float v, const Epilogue& ep, int
   return v;
 }
 
+// ------------------------------------------------------------------ large-M kernel
+//
+// Prefill shapes (M = 48 x 512 rows) use a 256 x 256 x 64 tile with 8 waves
+// (2 x 4, 128 x 64 each) and a software pipeline that keeps the matrix cores fed:
+// while the MFMAs of k-tile kt run from LDS stage kt % 2, the same waves write
+// k-tile kt+1 (already in registers) into the other stage -- A tile copied, W tile
+// dequantized on the way -- and issue the global loads of k-tile kt+2 as soon as
+// the registers they overwrite have been stored.  One barrier per k-tile.
+// Work-groups are remapped so that each XCD (the dispatcher deals work-groups to
+// the 8 XCDs round-robin) gets a contiguous run of tiles, walked in groups of 8
+// M-tiles, so the A rows and W columns that concurrently running tiles share stay
+// in that XCD's L2.
+__device__ __forceinline__ void big_tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+  constexpr int G = 8;
+  const int per_group = G * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * G;
+  const int gsize = min(tiles_m - first_m, G);
+  const int r = bid - group * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+// One 32-code piece of a W row (a 16-B load), dequantized into LDS chunk `chunk`.
+__device__ __forceinline__ void big_store_b_word(f16* b, int row, int chunk, uint32_t w, f16x2 s2,
+                                                 f16x2 m2) {
+  uint32_t pr[4];
+  codes_to_magic_pairs(w, pr);
+  uint4 o;
+  o.x = u32_from_h2(dequant_pair(pr[0], s2, m2));
+  o.y = u32_from_h2(dequant_pair(pr[1], s2, m2));
+  o.z = u32_from_h2(dequant_pair(pr[2], s2, m2));
+  o.w = u32_from_h2(dequant_pair(pr[3], s2, m2));
+  *(uint4*)(b + lds_off(row, chunk)) = o;
+}
+
 template <int WM, int WN, int TM, int TN, int OUT>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
     const f16* __restrict__ X, const uint8_t* __restrict__ Wc, const uint32_t* __restrict__ Wp,
     int M, int N, int K, int kt_per_split, Epilogue ep, void* __restrict__ Y) {
   using S = GemmShape<WM, WN, TM, TN>;
+  constexpr int AJ = S::A_PER_T;           // 16-B A chunks per thread and k-tile
+  constexpr int BJ = S::B_PER_T;           // 16-B W code pieces per thread and k-tile
+  constexpr int AROWS = S::THREADS / 8;    // rows covered by one pass of A loads
+  constexpr int BROWS = S::THREADS / 2;    // W rows covered by one pass of B loads
+  static_assert(S::A_CHUNKS % S::THREADS == 0 && S::B_PIECES % S::THREADS == 0, "tile split");
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
-  f16* sA = smem;                       // [2][BM*64]
-  f16* sB = smem + 2 * S::BM * kBK;     // [2][BN*64]
+  f16* const sA = smem;                       // [2][BM*64]
+  f16* const sB = smem + 2 * S::BM * kBK;     // [2][BN*64]
+  constexpr int kStageA = S::BM * kBK, kStageB = S::BN * kBK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * S::BM;
-  const int n0 = blockIdx.x * S::BN;
+  int tm, tn;
+  big_tile_coords((M + S::BM - 1) / S::BM, (N + S::BN - 1) / S::BN, tm, tn);
+  const int m0 = tm * S::BM, n0 = tn * S::BN;
   const int KT = K / kBK;
-  const int kt0 = blockIdx.z * kt_per_split;
+  const int kt0 = blockIdx.y * kt_per_split;
   const int kt1 = min(KT, kt0 + kt_per_split);
   const int64_t ldc = K / 2, ldp = K / kBK;
 
-  uint4 ra[S::A_PER_T];
-  uint4 rb[S::B_PER_T];
-  uint32_t rp[S::B_PER_T];
+  // A: thread t copies chunk (t & 7) of tile rows (t >> 3) + AROWS j.  Rows past M
+  // read the tile's first row instead and are never stored, so every load stays in
+  // bounds without a branch; the same holds for W rows past N.
+  const int a_row = tid >> 3, a_ch = tid & 7;
+  // per-thread state lives in named scalars (the compiler keeps arrays of them in
+  // scratch memory); FLEXQ_BIG_FOR8 stamps out the eight possible copies and
+  // `if constexpr` drops the ones a tile shape does not use
+#define FLEXQ_BIG_FOR8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
+#define FLEXQ_BIG_FOR2(X) X(0) X(1)
+#define A_DECL(j)                                                              \
+  const f16* a_src##j = nullptr;                                               \
+  uint4 ra##j = make_uint4(0, 0, 0, 0);                                        \
+  if constexpr (j < AJ) {                                                      \
+    const int gm = m0 + a_row + AROWS * j;                                     \
+    a_src##j = X + (int64_t)(gm < M ? gm : m0) * K + a_ch * 8;                 \
+  }
+  FLEXQ_BIG_FOR8(A_DECL)
+#undef A_DECL
+  // lds_off(row + AROWS j, ch) = lds_off(row, ch) + AROWS j * 64 (AROWS is a multiple of 16)
+  const int a_lds0 = lds_off(a_row, a_ch);
+  // B: thread t expands 32 codes of W row (t >> 1) + BROWS j, half (t & 1) of the group.
+  const int b_row = tid >> 1, b_half = tid & 1;
+#define B_DECL(j)                                                              \
+  const uint8_t* b_src##j = nullptr;                                           \
+  const uint32_t* p_src##j = nullptr;                                          \
+  uint4 rb##j = make_uint4(0, 0, 0, 0);                                        \
+  uint32_t rp##j = 0;                                                          \
+  if constexpr (j < BJ) {                                                      \
+    const int gn0 = n0 + b_row + BROWS * j;                                    \
+    const int gn = gn0 < N ? gn0 : n0;                                         \
+    b_src##j = Wc + (int64_t)gn * ldc + b_half * 16;                           \
+    p_src##j = Wp + (int64_t)gn * ldp;                                         \
+  }
+  FLEXQ_BIG_FOR2(B_DECL)
+#undef B_DECL
 
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < S::A_PER_T; ++j) {
-      const int idx = tid + j * S::THREADS;
-      const int row = idx >> 3, ch = idx & 7;
-      const int gm = m0 + row;
-      ra[j] = (idx < S::A_CHUNKS && gm < M)
-                  ? *(const uint4*)(X + (int64_t)gm * K + kt * kBK + ch * 8)
-                  : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < S::B_PER_T; ++j) {
-      const int idx = tid + j * S::THREADS;
-      const int row = idx >> 1, half = idx & 1;
-      const int gn = n0 + row;
-      if (idx < S::B_PIECES && gn < N) {
-        rb[j] = *(const uint4*)(Wc + (int64_t)gn * ldc + kt * 32 + half * 16);
-        rp[j] = Wp[(int64_t)gn * ldp + kt];
-      } else {
-        rb[j] = make_uint4(0, 0, 0, 0);
-        rp[j] = 0;
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    f16* a = sA + buf * S::BM * kBK;
-    f16* b = sB + buf * S::BN * kBK;
-#pragma unroll
-    for (int j = 0; j < S::A_PER_T; ++j) {
-      const int idx = tid + j * S::THREADS;
-      if (idx < S::A_CHUNKS) *(uint4*)(a + lds_off(idx >> 3, idx & 7)) = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < S::B_PER_T; ++j) {
-      const int idx = tid + j * S::THREADS;
-      if (idx < S::B_PIECES) {
-        const int row = idx >> 1, half = idx & 1;
-        const f16x2 m2 = h2_from_u32((rp[j] & 0xFFFFu) * 0x10001u);
-        const f16x2 s2 = h2_from_u32((rp[j] >> 16) * 0x10001u);
-        const uint32_t w[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t pr[4];
-          codes_to_magic_pairs(w[q], pr);
-          uint4 o;
-          o.x = u32_from_h2(dequant_pair(pr[0], s2, m2));
-          o.y = u32_from_h2(dequant_pair(pr[1], s2, m2));
-          o.z = u32_from_h2(dequant_pair(pr[2], s2, m2));
-          o.w = u32_from_h2(dequant_pair(pr[3], s2, m2));
-          *(uint4*)(b + lds_off(row, half * 4 + q)) = o;
-        }
-      }
-    }
-  };
+#define A_LD(j) if constexpr (j < AJ) ra##j = *(const uint4*)(a_src##j + _o);
+#define BIG_LOAD_A(kt)                                                         \
+  do {                                                                         \
+    const int64_t _o = (int64_t)(kt) * kBK;                                    \
+    FLEXQ_BIG_FOR8(A_LD)                                                       \
+  } while (0)
+#define B_LD(j)                                                                \
+  if constexpr (j < BJ) {                                                      \
+    rb##j = *(const uint4*)(b_src##j + _kt * 32);                              \
+    rp##j = p_src##j[_kt];                                                     \
+  }
+#define BIG_LOAD_B(kt)                                                         \
+  do {                                                                         \
+    const int64_t _kt = (kt);                                                  \
+    FLEXQ_BIG_FOR2(B_LD)                                                       \
+  } while (0)
+#define A_ST(j) if constexpr (j < AJ) *(uint4*)(_a + AROWS * 64 * j) = ra##j;
+#define BIG_STORE_A(buf)                                                       \
+  do {                                                                         \
+    f16* _a = sA + (buf) * kStageA + a_lds0;                                   \
+    FLEXQ_BIG_FOR8(A_ST)                                                       \
+  } while (0)
+#define B_ST(j)                                                                \
+  if constexpr (j < BJ) {                                                      \
+    const uint32_t _w = _q == 0 ? rb##j.x : _q == 1 ? rb##j.y : _q == 2 ? rb##j.z : rb##j.w; \
+    big_store_b_word(sB + _buf * kStageB, b_row + BROWS * j, b_half * 4 + _q, _w, \
+                     h2_from_u32((rp##j >> 16) * 0x10001u),                    \
+                     h2_from_u32((rp##j & 0xFFFFu) * 0x10001u));               \
+  }
+#define BIG_STORE_B(buf, q)                                                    \
+  do {                                                                         \
+    const int _buf = (buf);                                                    \
+    constexpr int _q = (q);                                                    \
+    FLEXQ_BIG_FOR2(B_ST)                                                       \
+  } while (0)
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -140,39 +202,98 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
 
+  const int a_frag_row = wm * TM * 32 + (lane & 31);
+  const int b_frag_row = wn * TN * 32 + (lane & 31);
+
+#define BIG_FRAGS(buf, ks, FA, FB)                                                      \
+  do {                                                                                  \
+    const f16* _a = sA + (buf) * kStageA;                                               \
+    const f16* _b = sB + (buf) * kStageB;                                               \
+    const int _ch = 2 * (ks) + (lane >> 5);                                             \
+    _Pragma("unroll") for (int _i = 0; _i < TM; ++_i)                                   \
+        FA[_i] = *(const f16x8*)(_a + lds_off(a_frag_row + _i * 32, _ch));              \
+    _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                                   \
+        FB[_j] = *(const f16x8*)(_b + lds_off(b_frag_row + _j * 32, _ch));              \
+  } while (0)
+#define BIG_MMA(FA, FB)                                                                 \
+  do {                                                                                  \
+    _Pragma("unroll") for (int _i = 0; _i < TM; ++_i)                                   \
+        _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                               \
+            acc[_i][_j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FA[_i], FB[_j],        \
+                                                                 acc[_i][_j], 0, 0, 0); \
+  } while (0)
+// interleave: one MFMA, one LDS read of the next step's fragments, ...
+#define BIG_INTERLEAVE()                                                                \
+  do {                                                                                  \
+    _Pragma("unroll") for (int _k = 0; _k < TM + TN; ++_k) {                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+    }                                                                                   \
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);                  \
+  } while (0)
+
+  // Pipeline loads and stores are unconditional (tile indices clamped to the last
+  // k-tile): branch-free bodies let the compiler count outstanding loads exactly,
+  // so each wait covers only the data it needs.  The stores of the last iteration
+  // fill the stage no one reads again.  LDS fragments are double-buffered: the
+  // reads for step ks+1 are issued between the MFMAs of step ks.  sched_barrier(0)
+  // keeps the scheduler from sinking the global loads to the end of the body.
   if (kt0 < kt1) {
-    load_tile(kt0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) load_tile(kt + 1);
-    const f16* a = sA + buf * S::BM * kBK;
-    const f16* b = sB + buf * S::BN * kBK;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      f16x8 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *(const f16x8*)(a + lds_off(wm * TM * 32 + i * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *(const f16x8*)(b + lds_off(wn * TN * 32 + j * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) store_tile(buf ^ 1);
+    const int klast = kt1 - 1;
+    BIG_LOAD_A(kt0);
+    BIG_LOAD_B(kt0);
+    BIG_STORE_A(0);
+    BIG_STORE_B(0, 0);
+    BIG_STORE_B(0, 1);
+    BIG_STORE_B(0, 2);
+    BIG_STORE_B(0, 3);
+    BIG_LOAD_A(min(kt0 + 1, klast));
+    BIG_LOAD_B(min(kt0 + 1, klast));
     __syncthreads();
+    f16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      const int k2 = min(kt + 2, klast);
+      BIG_FRAGS(buf, 0, fa0, fb0);
+      BIG_FRAGS(buf, 1, fa1, fb1);
+      BIG_MMA(fa0, fb0);
+      BIG_INTERLEAVE();
+      __builtin_amdgcn_sched_barrier(0);
+      BIG_STORE_A(buf ^ 1);
+      BIG_LOAD_A(k2);
+      __builtin_amdgcn_sched_barrier(0);
+      BIG_FRAGS(buf, 2, fa0, fb0);
+      BIG_MMA(fa1, fb1);
+      BIG_INTERLEAVE();
+      __builtin_amdgcn_sched_barrier(0);
+      BIG_STORE_B(buf ^ 1, 0);
+      BIG_STORE_B(buf ^ 1, 1);
+      BIG_FRAGS(buf, 3, fa1, fb1);
+      BIG_MMA(fa0, fb0);
+      BIG_INTERLEAVE();
+      __builtin_amdgcn_sched_barrier(0);
+      BIG_STORE_B(buf ^ 1, 2);
+      BIG_STORE_B(buf ^ 1, 3);
+      BIG_LOAD_B(k2);
+      __builtin_amdgcn_sched_barrier(0);
+      BIG_MMA(fa1, fb1);
+      __syncthreads();
+    }
   }
+#undef BIG_LOAD_A
+#undef BIG_LOAD_B
+#undef BIG_STORE_A
+#undef BIG_STORE_B
+#undef A_LD
+#undef B_LD
+#undef A_ST
+#undef B_ST
+#undef FLEXQ_BIG_FOR8
+#undef FLEXQ_BIG_FOR2
+#undef BIG_FRAGS
+#undef BIG_MMA
+#undef BIG_INTERLEAVE
 
-  // accumulator (i, j, r) of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32 of tile (i, j)
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -188,7 +309,209 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_w4_kernel(
           } else if constexpr (OUT == kOutF32) {
             ((float*)Y)[(int64_t)row * N + col] = v;
           } else {
-            ((float*)Y)[((int64_t)blockIdx.z * M + row) * N + col] = v;
+            ((float*)Y)[((int64_t)blockIdx.y * M + row) * N + col] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ small-M kernel
+//
+// Decode shapes (M <= 160 rows: the whole batch of one step) are weight-streaming:
+// every W element is used by exactly one wave, so W never goes through LDS.  Each
+// wave owns TN x 32 output columns and loads its own codes straight into registers,
+// two k-tiles ahead; only the activation tile (M x 64) is staged in LDS and shared.
+// The k index inside a 64-wide k-tile is permuted so that one 16-B code load per
+// lane is exactly its MFMA B operand for all four k-steps: in k-step ks, lane l
+// (lane group g = l / 32) holds k = 32 g + 8 ks + e, e = 0..7.  The A operand is
+// read from LDS with the same numbering (chunk 4 g + ks of the row), so every
+// product pairs matching k.
+template <int MT, int NW, int TN>
+struct SkinnyShape {
+  static constexpr int BM = MT * 32;
+  static constexpr int BN = NW * TN * 32;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int A_CHUNKS = BM * 8;
+  static constexpr int A_PER_T = (A_CHUNKS + THREADS - 1) / THREADS;
+  static constexpr size_t LDS_BYTES = 2 * (size_t)BM * kBK * sizeof(f16);
+};
+
+template <int MT, int NW, int TN, int OUT>
+__global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
+    const f16* __restrict__ X, const uint8_t* __restrict__ Wc, const uint32_t* __restrict__ Wp,
+    int M, int N, int K, int kt_per_split, Epilogue ep, void* __restrict__ Y) {
+  using S = SkinnyShape<MT, NW, TN>;
+  static_assert(S::A_PER_T <= 8 && TN <= 2, "per-thread copies are stamped out for <= 8 / 2");
+  extern __shared__ __attribute__((aligned(16))) f16 smem[];
+  constexpr int kStageA = S::BM * kBK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int n0 = blockIdx.x * S::BN;
+  const int m0 = blockIdx.z * S::BM;
+  const int KT = K / kBK;
+  const int kt0 = blockIdx.y * kt_per_split;
+  const int kt1 = min(KT, kt0 + kt_per_split);
+  const int64_t ldc = K / 2, ldp = K / kBK;
+
+#define FLEXQ_SK_FOR8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
+#define FLEXQ_SK_FOR2(X) X(0) X(1)
+  // A: thread t copies chunk t of the tile (row t/8, chunk t%8) and every THREADS-th
+  // after it.  Rows past M read row 0 and are never stored.
+#define A_DECL(j)                                                              \
+  const f16* a_src##j = X;                                                     \
+  int a_lds##j = 0;                                                            \
+  bool a_on##j = false;                                                        \
+  uint4 ra##j = make_uint4(0, 0, 0, 0);                                        \
+  if constexpr (j < S::A_PER_T) {                                              \
+    const int idx = tid + j * S::THREADS;                                      \
+    a_on##j = idx < S::A_CHUNKS;                                               \
+    const int row = a_on##j ? idx >> 3 : 0, ch = idx & 7;                      \
+    a_src##j = X + (int64_t)(m0 + row < M ? m0 + row : m0) * K + ch * 8;       \
+    a_lds##j = lds_off(row, ch);                                               \
+  }
+  FLEXQ_SK_FOR8(A_DECL)
+#undef A_DECL
+  // B: lane l of wave w reads 16 B (32 codes, k = 32 g .. 32 g + 31 of the k-tile) of
+  // W row n0 + (w TN + j) 32 + l % 32, and that row's (offset, scale) word.
+#define B_DECL(j)                                                              \
+  const uint8_t* b_src##j = Wc;                                                \
+  const uint32_t* p_src##j = Wp;                                               \
+  if constexpr (j < TN) {                                                      \
+    const int gn0 = n0 + (wave * TN + j) * 32 + (lane & 31);                   \
+    const int gn = gn0 < N ? gn0 : 0;                                          \
+    b_src##j = Wc + (int64_t)gn * ldc + g * 16;                                \
+    p_src##j = Wp + (int64_t)gn * ldp;                                         \
+  }
+  FLEXQ_SK_FOR2(B_DECL)
+#undef B_DECL
+  uint4 rb0a = make_uint4(0, 0, 0, 0), rb1a = rb0a, rb0b = rb0a, rb1b = rb0a;
+  uint32_t rp0a = 0, rp1a = 0, rp0b = 0, rp1b = 0;
+
+#define A_LD(j) if constexpr (j < S::A_PER_T) { if (a_on##j) ra##j = *(const uint4*)(a_src##j + _o); }
+#define SK_LOAD_A(kt)                                                          \
+  do {                                                                         \
+    const int64_t _o = (int64_t)(kt) * kBK;                                    \
+    FLEXQ_SK_FOR8(A_LD)                                                        \
+  } while (0)
+#define A_ST(j) if constexpr (j < S::A_PER_T) { if (a_on##j) *(uint4*)(_a + a_lds##j) = ra##j; }
+#define SK_STORE_A(buf)                                                        \
+  do {                                                                         \
+    f16* _a = smem + (buf) * kStageA;                                          \
+    FLEXQ_SK_FOR8(A_ST)                                                        \
+  } while (0)
+#define SK_LOAD_B(kt, SET)                                                     \
+  do {                                                                         \
+    const int64_t _kt = (kt);                                                  \
+    rb0##SET = *(const uint4*)(b_src0 + _kt * 32);                             \
+    rp0##SET = p_src0[_kt];                                                    \
+    if constexpr (TN > 1) {                                                    \
+      rb1##SET = *(const uint4*)(b_src1 + _kt * 32);                           \
+      rp1##SET = p_src1[_kt];                                                  \
+    }                                                                          \
+  } while (0)
+
+  f32x16 acc[MT][TN];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
+
+  // one k-tile of MFMAs from LDS stage `buf` and B codes in set SET
+#define SK_COMPUTE(buf, SET)                                                              \
+  do {                                                                                    \
+    const f16* _a = smem + (buf) * kStageA;                                               \
+    const f16x2 _m0 = h2_from_u32((rp0##SET & 0xFFFFu) * 0x10001u);                       \
+    const f16x2 _s0 = h2_from_u32((rp0##SET >> 16) * 0x10001u);                           \
+    const f16x2 _m1 = h2_from_u32((rp1##SET & 0xFFFFu) * 0x10001u);                       \
+    const f16x2 _s1 = h2_from_u32((rp1##SET >> 16) * 0x10001u);                           \
+    const uint32_t _w0[4] = {rb0##SET.x, rb0##SET.y, rb0##SET.z, rb0##SET.w};             \
+    const uint32_t _w1[4] = {rb1##SET.x, rb1##SET.y, rb1##SET.z, rb1##SET.w};             \
+    _Pragma("unroll") for (int _ks = 0; _ks < 4; ++_ks) {                                 \
+      f16x8 _fb[TN];                                                                      \
+      {                                                                                   \
+        uint32_t _pr[4];                                                                  \
+        codes_to_magic_pairs(_w0[_ks], _pr);                                              \
+        _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
+          const f16x2 _d = dequant_pair(_pr[_e], _s0, _m0);                               \
+          _fb[0][2 * _e] = _d.x;                                                          \
+          _fb[0][2 * _e + 1] = _d.y;                                                      \
+        }                                                                                 \
+      }                                                                                   \
+      if constexpr (TN > 1) {                                                             \
+        uint32_t _pr[4];                                                                  \
+        codes_to_magic_pairs(_w1[_ks], _pr);                                              \
+        _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
+          const f16x2 _d = dequant_pair(_pr[_e], _s1, _m1);                               \
+          _fb[TN - 1][2 * _e] = _d.x;                                                     \
+          _fb[TN - 1][2 * _e + 1] = _d.y;                                                 \
+        }                                                                                 \
+      }                                                                                   \
+      _Pragma("unroll") for (int _i = 0; _i < MT; ++_i) {                                 \
+        const f16x8 _fa = *(const f16x8*)(_a + lds_off(_i * 32 + (lane & 31), 4 * g + _ks)); \
+        _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                                 \
+            acc[_i][_j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(_fa, _fb[_j], acc[_i][_j], 0, 0, 0); \
+      }                                                                                   \
+    }                                                                                     \
+  } while (0)
+
+  // Branch-free pipeline (tile indices clamped to the last k-tile): A is one k-tile
+  // ahead in registers and LDS, B two k-tiles ahead in two register sets.  The loop
+  // body covers two k-tiles so that the register sets keep fixed names.
+  if (kt0 < kt1) {
+    const int klast = kt1 - 1;
+    SK_LOAD_A(kt0);
+    SK_LOAD_B(kt0, a);
+    SK_LOAD_B(min(kt0 + 1, klast), b);
+    SK_STORE_A(0);
+    SK_LOAD_A(min(kt0 + 1, klast));
+    __syncthreads();
+    int kt = kt0;
+    for (; kt + 1 < kt1; kt += 2) {
+      // k-tile kt: LDS stage 0, B set a
+      SK_STORE_A(1);
+      SK_LOAD_A(min(kt + 2, klast));
+      SK_COMPUTE(0, a);
+      SK_LOAD_B(min(kt + 2, klast), a);
+      __syncthreads();
+      // k-tile kt + 1: LDS stage 1, B set b
+      SK_STORE_A(0);
+      SK_LOAD_A(min(kt + 3, klast));
+      SK_COMPUTE(1, b);
+      SK_LOAD_B(min(kt + 3, klast), b);
+      __syncthreads();
+    }
+    if (kt < kt1) SK_COMPUTE(0, a);
+  }
+#undef SK_COMPUTE
+#undef SK_LOAD_B
+#undef SK_STORE_A
+#undef SK_LOAD_A
+#undef A_ST
+#undef A_LD
+#undef FLEXQ_SK_FOR8
+#undef FLEXQ_SK_FOR2
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + (wave * TN + j) * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < M && col < N) {
+          const float v = acc[i][j][r];
+          if constexpr (OUT == kOutF16) {
+            ((f16*)Y)[(int64_t)row * N + col] = (f16)epilogue_value(v, ep, row, col, N);
+          } else if constexpr (OUT == kOutF32) {
+            ((float*)Y)[(int64_t)row * N + col] = v;
+          } else {
+            ((float*)Y)[((int64_t)blockIdx.y * M + row) * N + col] = v;
           }
         }
       }
@@ -227,32 +550,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // ------------------------------------------------------------------ host dispatch
 
 struct Plan {
-  int cfg;      // which tile shape
+  int cfg;      // which kernel / tile shape
   int bm, bn;
   int splits;
   int kt_per_split;
 };
 
-constexpr int kCfgPrefill = 0;  // 256 x 256, 2x4 waves of 128x64 (8 waves, 2 per SIMD)
-constexpr int kCfgM32 = 1;      // 32 x 128
-constexpr int kCfgM64 = 2;      // 64 x 128
-constexpr int kCfgM160 = 3;     // 160 x 128
+constexpr int kCfgBig = 0;      // M > 160: 256 x 256 tile, 8 waves (pipelined, dequant into LDS)
+constexpr int kCfgSkinny = 1;   // M <= 160: 32*ceil(M/32) x 256 tile, W streamed to registers
 
 static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   Plan p;
-  if (M <= 32) { p.cfg = kCfgM32; p.bm = 32; p.bn = 128; }
-  else if (M <= 64) { p.cfg = kCfgM64; p.bm = 64; p.bn = 128; }
-  else if (M <= 160) { p.cfg = kCfgM160; p.bm = 160; p.bn = 128; }
-  else { p.cfg = kCfgPrefill; p.bm = 256; p.bn = 256; }
+  if (M <= 160) { p.cfg = kCfgSkinny; p.bm = (int)((M + 31) / 32) * 32; p.bn = 256; }
+  else { p.cfg = kCfgBig; p.bm = 256; p.bn = 256; }
   const int64_t KT = K / kBK;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int splits = 1;
-  // too few work-groups for 256 CUs: split K (fixed rule, so results only depend on
+  // too few work-groups for 256 CUs: split K (a fixed rule, so results depend only on
   // the shape and on whether the workspace is large enough)
   if (tiles < 512) {
     splits = (int)((512 + tiles - 1) / tiles);
     splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, KT / 8));
-    splits = std::min(splits, 16);
+    // the small-M kernel streams W once; beyond 4 splits its partial sums cost more
+    // traffic than the extra work-groups win (measured on the OPT-175B decode shapes)
+    splits = std::min(splits, p.cfg == kCfgSkinny ? 4 : 16);
   }
   if ((M * N) % 4) splits = 1;
   while (splits > 1 && (size_t)splits * M * N * sizeof(float) > ws_bytes) --splits;
@@ -263,18 +584,31 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
 }
 
 template <int WM, int WN, int TM, int TN, int OUT>
-static void launch_cfg(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
+static void launch_big(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
                        void* Y, hipStream_t stream) {
   using S = GemmShape<WM, WN, TM, TN>;
-  auto kern = gemm_w4_kernel<WM, WN, TM, TN, OUT>;
+  auto kern = gemm_w4_big_kernel<WM, WN, TM, TN, OUT>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)S::LDS_BYTES);
+                              (int)S::LDS_BYTES);
     attr_set = true;
   }
   const int N = (int)W->rows, K = (int)W->cols;
-  dim3 grid((N + S::BN - 1) / S::BN, (M + S::BM - 1) / S::BM, p.splits);
+  const int tiles = ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
+  dim3 grid(tiles, p.splits);
+  hipLaunchKernelGGL(kern, grid, dim3(S::THREADS), S::LDS_BYTES, stream, x, W->codes,
+                     (const uint32_t*)W->params, M, N, K, p.kt_per_split, ep, Y);
+}
+
+template <int MT, int OUT>
+static void launch_skinny(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
+                          void* Y, hipStream_t stream) {
+  constexpr int NW = 4, TN = 2;
+  using S = SkinnyShape<MT, NW, TN>;
+  auto kern = gemm_w4_skinny_kernel<MT, NW, TN, OUT>;
+  const int N = (int)W->rows, K = (int)W->cols;
+  dim3 grid((N + S::BN - 1) / S::BN, p.splits, (M + S::BM - 1) / S::BM);
   hipLaunchKernelGGL(kern, grid, dim3(S::THREADS), S::LDS_BYTES, stream, x, W->codes,
                      (const uint32_t*)W->params, M, N, K, p.kt_per_split, ep, Y);
 }
@@ -282,11 +616,16 @@ static void launch_cfg(const Plan& p, const f16* x, const flexq_w4* W, int M, Ep
 template <int OUT>
 static void launch_plan(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
                         void* Y, hipStream_t stream) {
-  switch (p.cfg) {
-    case kCfgM32: launch_cfg<1, 4, 1, 1, OUT>(p, x, W, M, ep, Y, stream); break;
-    case kCfgM64: launch_cfg<1, 4, 2, 1, OUT>(p, x, W, M, ep, Y, stream); break;
-    case kCfgM160: launch_cfg<1, 4, 5, 1, OUT>(p, x, W, M, ep, Y, stream); break;
-    default: launch_cfg<2, 4, 4, 2, OUT>(p, x, W, M, ep, Y, stream); break;
+  if (p.cfg == kCfgSkinny) {
+    switch (p.bm / 32) {
+      case 1: launch_skinny<1, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 2: launch_skinny<2, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 3: launch_skinny<3, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 4: launch_skinny<4, OUT>(p, x, W, M, ep, Y, stream); break;
+      default: launch_skinny<5, OUT>(p, x, W, M, ep, Y, stream); break;
+    }
+  } else {
+    launch_big<2, 4, 4, 2, OUT>(p, x, W, M, ep, Y, stream);
   }
 }
 

@@ -6,6 +6,11 @@
     python -m group_wise_bit_flexq_amd.kernel_probe decode --workload opt175b --reps 2
         one decode step's 4-bit GEMMs (M = batch) and decode attention over a cache
         of prompt + gen/2 positions;
+    python -m group_wise_bit_flexq_amd.kernel_probe quant --reps 3
+        the standalone quantizer on a 4 GiB fp16 tensor [524288][4096];
+    python -m group_wise_bit_flexq_amd.kernel_probe stress --reps 3
+        decode attention of the KV-compression stress shape (batch 64, 56 heads x 128,
+        cache of 2048 + 64 positions);
     python -m group_wise_bit_flexq_amd.kernel_probe copy --mib 1024 --reps 3
         an elementwise device copy of a known size, the reference that scales the
         HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above.
@@ -74,6 +79,37 @@ def decode(wl, reps):
     return res
 
 
+def quant(reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    from group_wise_bit_flexq_amd.workloads import QUANT_4GIB
+    rows, cols = QUANT_4GIB["rows"], QUANT_4GIB["cols"]
+    x = synth.normal_fp16((rows, cols), 1.0, 5, device="cuda")
+    w = F.W4.empty(rows, cols)
+    ms = _time(lambda: F.quantize(x, out=w), reps)
+    nbytes = rows * cols * 2.5625
+    return {"elements": rows * cols, "ms": ms, "gbps": nbytes / ms / 1e6}
+
+
+def stress(reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd.workloads import KV_STRESS as c
+    B, nh, hd = c["batch"], c["heads"], c["head_dim"]
+    T = c["prompt"] + c["steps"] - 1
+    kv = F.KV4(B, nh, hd, T + 1)
+    qkv = torch.randn(B, 3 * nh * hd, device="cuda").half()
+    out = torch.empty(B, nh * hd, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(F.attn_decode_ws_bytes(B, nh, hd, T), 16), dtype=torch.uint8,
+                     device="cuda")
+    ms = _time(lambda: F.attn_decode(qkv, T, kv, out=out, ws=ws), reps)
+    nbytes = B * nh * (T + 1) * 2 * hd * 0.5625
+    return {"T": T + 1, "ms": ms, "gbps": nbytes / ms / 1e6}
+
+
 def copy(mib, reps):
     import torch
     n = mib * (1 << 20) // 2
@@ -85,7 +121,7 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "quant", "stress", "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -98,6 +134,10 @@ def main():
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
+    elif a.what == "quant":
+        r = quant(a.reps)
+    elif a.what == "stress":
+        r = stress(a.reps)
     else:
         r = copy(a.mib, a.reps)
     print(json.dumps({"probe": a.what, "workload": a.workload, "results": r}), flush=True)
