@@ -56,23 +56,38 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Expand 8 packed 4-bit codes (one 32-bit word, element 2j in the low nibble of
-// byte j) to four fp16 pairs holding (1024 + c): the code sits in the low mantissa
-// bits of 0x6400 = 1024.0.  Pair j holds elements (2j, 2j+1).
-__device__ __forceinline__ void codes_to_magic_pairs(uint32_t w, uint32_t out[4]) {
+// Exact fp16 values of the codes in two bytes of `t` (bytes 0-1, or 2-3 when HI): a
+// code zero-extended to a byte is the OCP FP8 E4M3 encoding of c * 2^-9 (subnormal
+// for c < 8, exponent field 1 for c >= 8), so the scaled FP8 -> F16 convert with
+// scale 2^9 returns c itself, with no rounding.
+template <bool HI>
+__device__ __forceinline__ f16x2 code_pair_f16(uint32_t t) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 512.0f, HI);
+}
+
+// Spread 8 packed 4-bit codes (one 32-bit word, element 2j in the low nibble of byte
+// j) to one code per byte: t0 = (c0, c1, c2, c3), t1 = (c4, c5, c6, c7).
+__device__ __forceinline__ void codes_to_bytes(uint32_t w, uint32_t& t0, uint32_t& t1) {
   const uint32_t lo = w & 0x0F0F0F0Fu;          // c0 c2 c4 c6 in bytes 0..3
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
-  // perm(S0=hi, S1=lo): selector bytes 0-3 pick lo bytes, 4-7 pick hi bytes, 0x0c -> 0
-  out[0] = __builtin_amdgcn_perm(hi, lo, 0x0c040c00u) | 0x64006400u;
-  out[1] = __builtin_amdgcn_perm(hi, lo, 0x0c050c01u) | 0x64006400u;
-  out[2] = __builtin_amdgcn_perm(hi, lo, 0x0c060c02u) | 0x64006400u;
-  out[3] = __builtin_amdgcn_perm(hi, lo, 0x0c070c03u) | 0x64006400u;
+  // perm(S0 = hi, S1 = lo): selector bytes 0-3 pick lo bytes, 4-7 pick hi bytes
+  t0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  t1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// The four exact code pairs (c_2j, c_2j+1), j = 0..3, of one packed word.
+__device__ __forceinline__ void codes_to_pairs(uint32_t w, f16x2 out[4]) {
+  uint32_t t0, t1;
+  codes_to_bytes(w, t0, t1);
+  out[0] = code_pair_f16<false>(t0);
+  out[1] = code_pair_f16<true>(t0);
+  out[2] = code_pair_f16<false>(t1);
+  out[3] = code_pair_f16<true>(t1);
 }
 
 // Weight dequantization of one code pair: fp16(c * s + m) with a single rounding
-// (fused multiply-add in fp16; c is exact after removing the 1024 bias).
-__device__ __forceinline__ f16x2 dequant_pair(uint32_t magic_pair, f16x2 s2, f16x2 m2) {
-  f16x2 c = h2_from_u32(magic_pair) - (f16x2){(f16)1024.0f, (f16)1024.0f};
+// (fused multiply-add in fp16 of exact operands).
+__device__ __forceinline__ f16x2 dequant_pair(f16x2 c, f16x2 s2, f16x2 m2) {
   return __builtin_elementwise_fma(c, s2, m2);
 }
 

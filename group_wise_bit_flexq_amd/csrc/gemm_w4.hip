@@ -64,17 +64,32 @@ __device__ __forceinline__ float epilogue_value(float v, const Epilogue& ep, int
 // (2 x 4, 128 x 64 each) and a software pipeline that keeps the matrix cores fed:
 // while the MFMAs of k-tile kt run from LDS stage kt % 2, the same waves write
 // k-tile kt+1 (already in registers) into the other stage -- A tile copied, W tile
-// dequantized on the way -- and issue the global loads of k-tile kt+2 as soon as
-// the registers they overwrite have been stored.  One barrier per k-tile.
-// Work-groups are remapped so that each XCD (the dispatcher deals work-groups to
-// the 8 XCDs round-robin) gets a contiguous run of tiles, walked in groups of 8
-// M-tiles, so the A rows and W columns that concurrently running tiles share stay
-// in that XCD's L2.
+// dequantized on the way -- and issue the global loads of k-tile kt+2.  One barrier
+// per k-tile.  On gfx950 independent VALU work only partly overlaps a running MFMA
+// and LDS writes are about 2.5x slower per byte than reads, so the loop is ordered by
+// hand: every MFMA is followed by a small pinned slice of the side work.
+//
+// Tile order: the dispatcher deals work-groups to the 8 XCDs round-robin, so XCD x
+// runs work-groups x, x + 8, ...  XCD x is given the N-tile range [x nx, (x+1) nx)
+// and walks it in groups of 8 M-tiles; at any moment all XCDs work on the same 8
+// M-tiles, whose A rows are then shared through the last-level cache instead of
+// being fetched from HBM by each XCD, and each XCD's own L2 holds the W columns and
+// A rows its ~32 resident tiles share.
 __device__ __forceinline__ void big_tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nblk = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
   constexpr int G = 8;
+  const int bid = blockIdx.x;
+  if (tiles_n % 8 == 0) {
+    const int x = bid & 7, q = bid >> 3, nx = tiles_n >> 3;
+    const int per_group = G * nx;
+    const int group = q / per_group;
+    const int first_m = group * G;
+    const int gsize = min(tiles_m - first_m, G);
+    const int r = q - group * per_group;
+    tm = first_m + r % gsize;
+    tn = x * nx + r / gsize;
+    return;
+  }
+  // other widths: plain groups of 8 M-tiles in launch order
   const int per_group = G * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * G;
@@ -82,19 +97,6 @@ __device__ __forceinline__ void big_tile_coords(int tiles_m, int tiles_n, int& t
   const int r = bid - group * per_group;
   tm = first_m + r % gsize;
   tn = r / gsize;
-}
-
-// One 32-code piece of a W row (a 16-B load), dequantized into LDS chunk `chunk`.
-__device__ __forceinline__ void big_store_b_word(f16* b, int row, int chunk, uint32_t w, f16x2 s2,
-                                                 f16x2 m2) {
-  uint32_t pr[4];
-  codes_to_magic_pairs(w, pr);
-  uint4 o;
-  o.x = u32_from_h2(dequant_pair(pr[0], s2, m2));
-  o.y = u32_from_h2(dequant_pair(pr[1], s2, m2));
-  o.z = u32_from_h2(dequant_pair(pr[2], s2, m2));
-  o.w = u32_from_h2(dequant_pair(pr[3], s2, m2));
-  *(uint4*)(b + lds_off(row, chunk)) = o;
 }
 
 template <int WM, int WN, int TM, int TN, int OUT>
@@ -105,7 +107,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
   constexpr int AJ = S::A_PER_T;           // 16-B A chunks per thread and k-tile
   constexpr int BJ = S::B_PER_T;           // 16-B W code pieces per thread and k-tile
   constexpr int AROWS = S::THREADS / 8;    // rows covered by one pass of A loads
-  constexpr int BROWS = S::THREADS / 2;    // W rows covered by one pass of B loads
   static_assert(S::A_CHUNKS % S::THREADS == 0 && S::B_PIECES % S::THREADS == 0, "tile split");
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   f16* const sA = smem;                       // [2][BM*64]
@@ -124,175 +125,164 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
   const int kt1 = min(KT, kt0 + kt_per_split);
   const int64_t ldc = K / 2, ldp = K / kBK;
 
-  // A: thread t copies chunk (t & 7) of tile rows (t >> 3) + AROWS j.  Rows past M
-  // read the tile's first row instead and are never stored, so every load stays in
-  // bounds without a branch; the same holds for W rows past N.
-  const int a_row = tid >> 3, a_ch = tid & 7;
-  // per-thread state lives in named scalars (the compiler keeps arrays of them in
-  // scratch memory); FLEXQ_BIG_FOR8 stamps out the eight possible copies and
-  // `if constexpr` drops the ones a tile shape does not use
-#define FLEXQ_BIG_FOR8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
-#define FLEXQ_BIG_FOR2(X) X(0) X(1)
-#define A_DECL(j)                                                              \
-  const f16* a_src##j = nullptr;                                               \
-  uint4 ra##j = make_uint4(0, 0, 0, 0);                                        \
-  if constexpr (j < AJ) {                                                      \
-    const int gm = m0 + a_row + AROWS * j;                                     \
-    a_src##j = X + (int64_t)(gm < M ? gm : m0) * K + a_ch * 8;                 \
-  }
-  FLEXQ_BIG_FOR8(A_DECL)
-#undef A_DECL
-  // lds_off(row + AROWS j, ch) = lds_off(row, ch) + AROWS j * 64 (AROWS is a multiple of 16)
-  const int a_lds0 = lds_off(a_row, a_ch);
-  // B: thread t expands 32 codes of W row (t >> 1) + BROWS j, half (t & 1) of the group.
-  const int b_row = tid >> 1, b_half = tid & 1;
-#define B_DECL(j)                                                              \
-  const uint8_t* b_src##j = nullptr;                                           \
-  const uint32_t* p_src##j = nullptr;                                          \
-  uint4 rb##j = make_uint4(0, 0, 0, 0);                                        \
-  uint32_t rp##j = 0;                                                          \
-  if constexpr (j < BJ) {                                                      \
-    const int gn0 = n0 + b_row + BROWS * j;                                    \
-    const int gn = gn0 < N ? gn0 : n0;                                         \
-    b_src##j = Wc + (int64_t)gn * ldc + b_half * 16;                           \
-    p_src##j = Wp + (int64_t)gn * ldp;                                         \
-  }
-  FLEXQ_BIG_FOR2(B_DECL)
-#undef B_DECL
+  // The k-loop below is written out by hand for the 256 x 256 tile of 8 waves (2 x 4),
+  // each wave owning 128 x 64 outputs as 4 x 2 MFMA tiles of 32 x 32.
+  static_assert(WM == 2 && WN == 4 && TM == 4 && TN == 2, "k-loop is written for this tile");
+  static_assert(AJ == 4 && BJ == 1, "per-thread share of the A and B tiles");
 
-#define A_LD(j) if constexpr (j < AJ) ra##j = *(const uint4*)(a_src##j + _o);
-#define BIG_LOAD_A(kt)                                                         \
-  do {                                                                         \
-    const int64_t _o = (int64_t)(kt) * kBK;                                    \
-    FLEXQ_BIG_FOR8(A_LD)                                                       \
-  } while (0)
-#define B_LD(j)                                                                \
-  if constexpr (j < BJ) {                                                      \
-    rb##j = *(const uint4*)(b_src##j + _kt * 32);                              \
-    rp##j = p_src##j[_kt];                                                     \
-  }
-#define BIG_LOAD_B(kt)                                                         \
-  do {                                                                         \
-    const int64_t _kt = (kt);                                                  \
-    FLEXQ_BIG_FOR2(B_LD)                                                       \
-  } while (0)
-#define A_ST(j) if constexpr (j < AJ) *(uint4*)(_a + AROWS * 64 * j) = ra##j;
-#define BIG_STORE_A(buf)                                                       \
-  do {                                                                         \
-    f16* _a = sA + (buf) * kStageA + a_lds0;                                   \
-    FLEXQ_BIG_FOR8(A_ST)                                                       \
-  } while (0)
-#define B_ST(j)                                                                \
-  if constexpr (j < BJ) {                                                      \
-    const uint32_t _w = _q == 0 ? rb##j.x : _q == 1 ? rb##j.y : _q == 2 ? rb##j.z : rb##j.w; \
-    big_store_b_word(sB + _buf * kStageB, b_row + BROWS * j, b_half * 4 + _q, _w, \
-                     h2_from_u32((rp##j >> 16) * 0x10001u),                    \
-                     h2_from_u32((rp##j & 0xFFFFu) * 0x10001u));               \
-  }
-#define BIG_STORE_B(buf, q)                                                    \
-  do {                                                                         \
-    const int _buf = (buf);                                                    \
-    constexpr int _q = (q);                                                    \
-    FLEXQ_BIG_FOR2(B_ST)                                                       \
-  } while (0)
+  // A: thread t copies chunk (t & 7) of tile rows (t >> 3) + 64 j, j = 0..3.  Rows past M
+  // read the tile's first row instead and are never stored, so every load stays in
+  // bounds without a branch; the same holds for W rows past N.  Per-thread state lives
+  // in named scalars: the compiler puts arrays of them in scratch memory.
+  const int a_row = tid >> 3, a_ch = tid & 7;
+#define A_SRC(j)                                                                         \
+  const f16* const a_src##j =                                                            \
+      X + (int64_t)(m0 + a_row + AROWS * j < M ? m0 + a_row + AROWS * j : m0) * K + a_ch * 8;
+  A_SRC(0) A_SRC(1) A_SRC(2) A_SRC(3)
+#undef A_SRC
+  // lds_off(row + 64 j, ch) = lds_off(row, ch) + 64 j * 64 (the swizzle sees row bits 1-3)
+  const int a_lds = lds_off(a_row, a_ch);
+  // B: thread t expands the 32 codes of W row t >> 1, half t & 1 of the 64-code group:
+  // word q of its 16-B piece becomes LDS chunk 4 (t & 1) + q of that row.
+  const int b_row = tid >> 1, b_half = tid & 1;
+  const int b_gn = n0 + b_row < N ? n0 + b_row : n0;
+  const uint8_t* const b_src = Wc + (int64_t)b_gn * ldc + b_half * 16;
+  const uint32_t* const p_src = Wp + (int64_t)b_gn * ldp;
+  const int b_lds0 = lds_off(b_row, b_half * 4 + 0), b_lds1 = lds_off(b_row, b_half * 4 + 1);
+  const int b_lds2 = lds_off(b_row, b_half * 4 + 2), b_lds3 = lds_off(b_row, b_half * 4 + 3);
+  uint4 ra0, ra1, ra2, ra3;         // A chunks of the next k-tile
+  uint4 rb_0, rb_1;                 // W codes, two k-tiles in flight (set = tile parity)
+  uint32_t rp_0, rp_1;              // their (offset, step) words
+  uint32_t dq_t0, dq_t1, dq0, dq1, dq2, dq3;
+  f16x2 dq_s, dq_m;
 
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
+  // fragment sets: k-steps alternate between set 0 and set 1
+  f16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
-  const int a_frag_row = wm * TM * 32 + (lane & 31);
-  const int b_frag_row = wn * TN * 32 + (lane & 31);
+  // Lane (l & 31) of a fragment is row (l & 31) of its 32-row slice; lane half l >> 5
+  // takes k 8 (l >> 5) .. +8 of the 16-wide k-step, i.e. LDS chunk 2 ks + (l >> 5).
+  // The swizzle term (row >> 1) & 7 is the same for every 32-row slice of the wave.
+  const int fa_row = wm * TM * 32 + (lane & 31), fb_row = wn * TN * 32 + (lane & 31);
+  const int fa_base = fa_row * 64, fb_base = fb_row * 64;
+  const int f_sw = (fa_row >> 1) & 7;    // == (fb_row >> 1) & 7: both rows are lane & 31 + 32 x
+  const int f_ch = lane >> 5;
 
-#define BIG_FRAGS(buf, ks, FA, FB)                                                      \
-  do {                                                                                  \
-    const f16* _a = sA + (buf) * kStageA;                                               \
-    const f16* _b = sB + (buf) * kStageB;                                               \
-    const int _ch = 2 * (ks) + (lane >> 5);                                             \
-    _Pragma("unroll") for (int _i = 0; _i < TM; ++_i)                                   \
-        FA[_i] = *(const f16x8*)(_a + lds_off(a_frag_row + _i * 32, _ch));              \
-    _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                                   \
-        FB[_j] = *(const f16x8*)(_b + lds_off(b_frag_row + _j * 32, _ch));              \
+#define SB() __builtin_amdgcn_sched_barrier(0)
+#define MF(FA, FB, i, j) \
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FA[i], FB[j], acc[i][j], 0, 0, 0)
+#define FRAG_A(F, BUF, KS, i) \
+  F[i] = *(const f16x8*)(sA + (BUF) * kStageA + fa_base + (i) * 32 * 64 + (((2 * (KS) + f_ch) ^ f_sw) << 3))
+#define FRAG_B(F, BUF, KS, j) \
+  F[j] = *(const f16x8*)(sB + (BUF) * kStageB + fb_base + (j) * 32 * 64 + (((2 * (KS) + f_ch) ^ f_sw) << 3))
+#define LOAD_A(j, KT) ra##j = *(const uint4*)(a_src##j + (int64_t)(KT) * kBK)
+#define STORE_A(j, BUF) *(uint4*)(sA + (BUF) * kStageA + a_lds + AROWS * 64 * j) = ra##j
+#define LOAD_B(SET, KT)                                   \
+  do {                                                    \
+    rb_##SET = *(const uint4*)(b_src + (int64_t)(KT) * 32); \
+    rp_##SET = p_src[KT];                                 \
   } while (0)
-#define BIG_MMA(FA, FB)                                                                 \
-  do {                                                                                  \
-    _Pragma("unroll") for (int _i = 0; _i < TM; ++_i)                                   \
-        _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                               \
-            acc[_i][_j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FA[_i], FB[_j],        \
-                                                                 acc[_i][_j], 0, 0, 0); \
+#define DQ_SCALE(SET)                                     \
+  do {                                                    \
+    dq_s = h2_from_u32((rp_##SET >> 16) * 0x10001u);      \
+    dq_m = h2_from_u32((rp_##SET & 0xFFFFu) * 0x10001u);  \
   } while (0)
-// interleave: one MFMA, one LDS read of the next step's fragments, ...
-#define BIG_INTERLEAVE()                                                                \
-  do {                                                                                  \
-    _Pragma("unroll") for (int _k = 0; _k < TM + TN; ++_k) {                            \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
-    }                                                                                   \
-    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - TM - TN, 0);                  \
+#define DQ_PRE(W) codes_to_bytes((W), dq_t0, dq_t1)
+// pair p of the word: elements 2p and 2p + 1
+#define DQ_PAIR(p) \
+  dq##p = u32_from_h2(dequant_pair(code_pair_f16<(p) & 1>((p) < 2 ? dq_t0 : dq_t1), dq_s, dq_m))
+#define STORE_B(q, BUF) *(uint4*)(sB + (BUF) * kStageB + b_lds##q) = make_uint4(dq0, dq1, dq2, dq3)
+
+// One k-step region: the 8 MFMAs of fragment set (FA, FB), each followed by a pinned
+// slice of side work so that the matrix core always has the next MFMA queued while
+// the wave issues VALU, LDS and global work: the 6 fragment reads of the next k-step
+// (set NA, NB, k-step KS of stage BUF), one A chunk of k-tile kt+1 (LDS stage NBUF),
+// one W word of it dequantized into stage NBUF, and the global load of A chunk R of
+// k-tile kt+2 (K2).  Region 0 also loads the W codes of k-tile kt+2 (set LSET) and
+// takes the scale of k-tile kt+1 (set USET).
+#define REGION(FA, FB, NA, NB, BUF, KS, R, WORD, NBUF, USET, LSET, K2) \
+  do {                                                                 \
+    MF(FA, FB, 0, 0); SB();                                            \
+    FRAG_A(NA, BUF, KS, 0); FRAG_B(NB, BUF, KS, 0); SB();              \
+    MF(FA, FB, 0, 1); SB();                                            \
+    FRAG_B(NB, BUF, KS, 1); STORE_A(R, NBUF); SB();                    \
+    MF(FA, FB, 1, 0); SB();                                            \
+    FRAG_A(NA, BUF, KS, 1); LOAD_A(R, K2);                             \
+    if ((R) == 0) { DQ_SCALE(USET); LOAD_B(LSET, K2); }                \
+    SB();                                                              \
+    MF(FA, FB, 1, 1); SB();                                            \
+    FRAG_A(NA, BUF, KS, 2); DQ_PRE(rb_##USET.WORD); DQ_PAIR(0); SB();  \
+    MF(FA, FB, 2, 0); SB();                                            \
+    FRAG_A(NA, BUF, KS, 3); DQ_PAIR(1); SB();                          \
+    MF(FA, FB, 2, 1); SB();                                            \
+    DQ_PAIR(2); SB();                                                  \
+    MF(FA, FB, 3, 0); SB();                                            \
+    DQ_PAIR(3); STORE_B(R, NBUF); SB();                                \
+    MF(FA, FB, 3, 1); SB();                                            \
+  } while (0)
+// One k-tile kt in LDS stage BUF (k-tile kt+1 goes to the other stage); region 0
+// finishes the previous k-tile's last k-step (all-zero fragments before the first).
+#define TILE(BUF, NBUF, KT)                                                           \
+  do {                                                                                \
+    const int _k2 = min((KT) + 2, klast);                                             \
+    REGION(fa1, fb1, fa0, fb0, BUF, 0, 0, x, NBUF, NBUF, BUF, _k2);                   \
+    REGION(fa0, fb0, fa1, fb1, BUF, 1, 1, y, NBUF, NBUF, BUF, _k2);                   \
+    REGION(fa1, fb1, fa0, fb0, BUF, 2, 2, z, NBUF, NBUF, BUF, _k2);                   \
+    REGION(fa0, fb0, fa1, fb1, BUF, 3, 3, w, NBUF, NBUF, BUF, _k2);                   \
+    __syncthreads();                                                                  \
   } while (0)
 
-  // Pipeline loads and stores are unconditional (tile indices clamped to the last
-  // k-tile): branch-free bodies let the compiler count outstanding loads exactly,
-  // so each wait covers only the data it needs.  The stores of the last iteration
-  // fill the stage no one reads again.  LDS fragments are double-buffered: the
-  // reads for step ks+1 are issued between the MFMAs of step ks.  sched_barrier(0)
-  // keeps the scheduler from sinking the global loads to the end of the body.
+  // Software pipeline over k-tiles.  While k-tile kt is multiplied out of LDS stage
+  // (kt - kt0) & 1, the same waves write k-tile kt+1 (registers -> the other stage, W
+  // dequantized on the way) and issue the global loads of k-tile kt+2; the k-steps are
+  // rotated by one so that MFMAs follow each barrier at once.  Loads and stores are
+  // unconditional (indices clamped to the last k-tile), which keeps the counts of
+  // outstanding loads exact; the final stores fill a stage no one reads.  The loop is
+  // unrolled by two so that stage offsets are constants.
   if (kt0 < kt1) {
     const int klast = kt1 - 1;
-    BIG_LOAD_A(kt0);
-    BIG_LOAD_B(kt0);
-    BIG_STORE_A(0);
-    BIG_STORE_B(0, 0);
-    BIG_STORE_B(0, 1);
-    BIG_STORE_B(0, 2);
-    BIG_STORE_B(0, 3);
-    BIG_LOAD_A(min(kt0 + 1, klast));
-    BIG_LOAD_B(min(kt0 + 1, klast));
+    const int k1 = min(kt0 + 1, klast);
+    LOAD_A(0, kt0); LOAD_A(1, kt0); LOAD_A(2, kt0); LOAD_A(3, kt0);
+    LOAD_B(0, kt0);
+    STORE_A(0, 0); STORE_A(1, 0); STORE_A(2, 0); STORE_A(3, 0);
+    DQ_SCALE(0);
+    DQ_PRE(rb_0.x); DQ_PAIR(0); DQ_PAIR(1); DQ_PAIR(2); DQ_PAIR(3); STORE_B(0, 0);
+    DQ_PRE(rb_0.y); DQ_PAIR(0); DQ_PAIR(1); DQ_PAIR(2); DQ_PAIR(3); STORE_B(1, 0);
+    DQ_PRE(rb_0.z); DQ_PAIR(0); DQ_PAIR(1); DQ_PAIR(2); DQ_PAIR(3); STORE_B(2, 0);
+    DQ_PRE(rb_0.w); DQ_PAIR(0); DQ_PAIR(1); DQ_PAIR(2); DQ_PAIR(3); STORE_B(3, 0);
+    LOAD_A(0, k1); LOAD_A(1, k1); LOAD_A(2, k1); LOAD_A(3, k1);
+    LOAD_B(1, k1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa1[i] = (f16x8){0};
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb1[j] = (f16x8){0};
     __syncthreads();
-    f16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
-      const int k2 = min(kt + 2, klast);
-      BIG_FRAGS(buf, 0, fa0, fb0);
-      BIG_FRAGS(buf, 1, fa1, fb1);
-      BIG_MMA(fa0, fb0);
-      BIG_INTERLEAVE();
-      __builtin_amdgcn_sched_barrier(0);
-      BIG_STORE_A(buf ^ 1);
-      BIG_LOAD_A(k2);
-      __builtin_amdgcn_sched_barrier(0);
-      BIG_FRAGS(buf, 2, fa0, fb0);
-      BIG_MMA(fa1, fb1);
-      BIG_INTERLEAVE();
-      __builtin_amdgcn_sched_barrier(0);
-      BIG_STORE_B(buf ^ 1, 0);
-      BIG_STORE_B(buf ^ 1, 1);
-      BIG_FRAGS(buf, 3, fa1, fb1);
-      BIG_MMA(fa0, fb0);
-      BIG_INTERLEAVE();
-      __builtin_amdgcn_sched_barrier(0);
-      BIG_STORE_B(buf ^ 1, 2);
-      BIG_STORE_B(buf ^ 1, 3);
-      BIG_LOAD_B(k2);
-      __builtin_amdgcn_sched_barrier(0);
-      BIG_MMA(fa1, fb1);
-      __syncthreads();
+    int kt = kt0;
+    for (; kt + 1 < kt1; kt += 2) {
+      TILE(0, 1, kt);
+      TILE(1, 0, kt + 1);
     }
+    if (kt < kt1) TILE(0, 1, kt);
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) MF(fa1, fb1, i, j);
   }
-#undef BIG_LOAD_A
-#undef BIG_LOAD_B
-#undef BIG_STORE_A
-#undef BIG_STORE_B
-#undef A_LD
-#undef B_LD
-#undef A_ST
-#undef B_ST
-#undef FLEXQ_BIG_FOR8
-#undef FLEXQ_BIG_FOR2
-#undef BIG_FRAGS
-#undef BIG_MMA
-#undef BIG_INTERLEAVE
+#undef SB
+#undef MF
+#undef FRAG_A
+#undef FRAG_B
+#undef LOAD_A
+#undef STORE_A
+#undef LOAD_B
+#undef DQ_SCALE
+#undef DQ_PRE
+#undef DQ_PAIR
+#undef STORE_B
+#undef REGION
+#undef TILE
 
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -434,8 +424,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
     _Pragma("unroll") for (int _ks = 0; _ks < 4; ++_ks) {                                 \
       f16x8 _fb[TN];                                                                      \
       {                                                                                   \
-        uint32_t _pr[4];                                                                  \
-        codes_to_magic_pairs(_w0[_ks], _pr);                                              \
+        f16x2 _pr[4];                                                                     \
+        codes_to_pairs(_w0[_ks], _pr);                                                    \
         _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
           const f16x2 _d = dequant_pair(_pr[_e], _s0, _m0);                               \
           _fb[0][2 * _e] = _d.x;                                                          \
@@ -443,8 +433,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
         }                                                                                 \
       }                                                                                   \
       if constexpr (TN > 1) {                                                             \
-        uint32_t _pr[4];                                                                  \
-        codes_to_magic_pairs(_w1[_ks], _pr);                                              \
+        f16x2 _pr[4];                                                                     \
+        codes_to_pairs(_w1[_ks], _pr);                                                    \
         _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
           const f16x2 _d = dequant_pair(_pr[_e], _s1, _m1);                               \
           _fb[TN - 1][2 * _e] = _d.x;                                                     \

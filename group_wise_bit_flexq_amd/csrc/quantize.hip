@@ -51,9 +51,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint2* __restrict
   const uint32_t p = params[i / 4];
   const f16x2 m2 = h2_from_u32((p & 0xFFFFu) * 0x10001u);
   const f16x2 s2 = h2_from_u32((p >> 16) * 0x10001u);
-  uint32_t pr[8];
-  codes_to_magic_pairs(c.x, pr);
-  codes_to_magic_pairs(c.y, pr + 4);
+  f16x2 pr[8];
+  codes_to_pairs(c.x, pr);
+  codes_to_pairs(c.y, pr + 4);
   uint32_t o[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = u32_from_h2(dequant_pair(pr[k], s2, m2));
