@@ -71,12 +71,13 @@ __device__ __forceinline__ float epilogue_value(float v, const Epilogue& ep, int
 //
 // Tile order: the dispatcher deals work-groups to the 8 XCDs round-robin, so XCD x
 // runs work-groups x, x + 8, ...  XCD x is given the N-tile range [x nx, (x+1) nx)
-// and walks it in groups of 8 M-tiles; at any moment all XCDs work on the same 8
+// and walks it in groups of 4 M-tiles; at any moment all XCDs work on the same 4
 // M-tiles, whose A rows are then shared through the last-level cache instead of
-// being fetched from HBM by each XCD, and each XCD's own L2 holds the W columns and
-// A rows its ~32 resident tiles share.
+// being fetched from HBM by each XCD, and the ~32 tiles resident on one XCD form a
+// 4 x 8 block whose A rows (32 KB per k-tile each) and W columns (9 KB) its L2
+// shares -- the shape with the fewest L2 misses for those sizes.
 __device__ __forceinline__ void big_tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int G = 8;
+  constexpr int G = 4;
   const int bid = blockIdx.x;
   if (tiles_n % 8 == 0) {
     const int x = bid & 7, q = bid >> 3, nx = tiles_n >> 3;
@@ -89,7 +90,7 @@ __device__ __forceinline__ void big_tile_coords(int tiles_m, int tiles_n, int& t
     tn = x * nx + r / gsize;
     return;
   }
-  // other widths: plain groups of 8 M-tiles in launch order
+  // other widths: plain groups of 4 M-tiles in launch order
   const int per_group = G * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * G;
