@@ -334,9 +334,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
     const f16* __restrict__ X, const uint8_t* __restrict__ Wc, const uint32_t* __restrict__ Wp,
     int M, int N, int K, int kt_per_split, Epilogue ep, void* __restrict__ Y) {
   using S = SkinnyShape<MT, NW, TN>;
-  static_assert(S::A_PER_T <= 8 && TN <= 2, "per-thread copies are stamped out for <= 8 / 2");
+  static_assert(NW == 4 && TN == 2 && MT >= 1 && MT <= 5, "k-loop is written for 4 waves x 64 columns");
+  static_assert(S::A_CHUNKS == MT * S::THREADS, "one A chunk per thread and 32 rows");
   extern __shared__ __attribute__((aligned(16))) f16 smem[];
   constexpr int kStageA = S::BM * kBK;
+  constexpr int NS = MT * TN;             // MFMAs (= side-work slices) per k-step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -349,143 +351,163 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
   const int kt1 = min(KT, kt0 + kt_per_split);
   const int64_t ldc = K / 2, ldp = K / kBK;
 
-#define FLEXQ_SK_FOR8(X) X(0) X(1) X(2) X(3) X(4) X(5) X(6) X(7)
-#define FLEXQ_SK_FOR2(X) X(0) X(1)
-  // A: thread t copies chunk t of the tile (row t/8, chunk t%8) and every THREADS-th
-  // after it.  Rows past M read row 0 and are never stored.
-#define A_DECL(j)                                                              \
-  const f16* a_src##j = X;                                                     \
-  int a_lds##j = 0;                                                            \
-  bool a_on##j = false;                                                        \
-  uint4 ra##j = make_uint4(0, 0, 0, 0);                                        \
-  if constexpr (j < S::A_PER_T) {                                              \
-    const int idx = tid + j * S::THREADS;                                      \
-    a_on##j = idx < S::A_CHUNKS;                                               \
-    const int row = a_on##j ? idx >> 3 : 0, ch = idx & 7;                      \
-    a_src##j = X + (int64_t)(m0 + row < M ? m0 + row : m0) * K + ch * 8;       \
-    a_lds##j = lds_off(row, ch);                                               \
-  }
-  FLEXQ_SK_FOR8(A_DECL)
-#undef A_DECL
+  // A: thread t copies chunk (t & 7) of tile rows (t >> 3) + 32 j, j < MT.  Rows past M
+  // read row m0 and are never stored.
+  const int a_row = tid >> 3, a_ch = tid & 7;
+#define A_SRC(j)                                                                        \
+  const f16* const a_src##j =                                                           \
+      X + (int64_t)(m0 + a_row + 32 * (j) < M ? m0 + a_row + 32 * (j) : m0) * K + a_ch * 8;
+  A_SRC(0) A_SRC(1) A_SRC(2) A_SRC(3) A_SRC(4)
+#undef A_SRC
+  const int a_lds = lds_off(a_row, a_ch);   // + 32 j * 64 for row + 32 j
+  // A chunks of two k-tiles in flight: set = (k-tile - kt0) & 1, the LDS stage it goes to
+  uint4 ra0_0, ra0_1, ra0_2, ra0_3, ra0_4, ra1_0, ra1_1, ra1_2, ra1_3, ra1_4;
   // B: lane l of wave w reads 16 B (32 codes, k = 32 g .. 32 g + 31 of the k-tile) of
-  // W row n0 + (w TN + j) 32 + l % 32, and that row's (offset, scale) word.
-#define B_DECL(j)                                                              \
-  const uint8_t* b_src##j = Wc;                                                \
-  const uint32_t* p_src##j = Wp;                                               \
-  if constexpr (j < TN) {                                                      \
-    const int gn0 = n0 + (wave * TN + j) * 32 + (lane & 31);                   \
-    const int gn = gn0 < N ? gn0 : 0;                                          \
-    b_src##j = Wc + (int64_t)gn * ldc + g * 16;                                \
-    p_src##j = Wp + (int64_t)gn * ldp;                                         \
-  }
-  FLEXQ_SK_FOR2(B_DECL)
-#undef B_DECL
-  uint4 rb0a = make_uint4(0, 0, 0, 0), rb1a = rb0a, rb0b = rb0a, rb1b = rb0a;
-  uint32_t rp0a = 0, rp1a = 0, rp0b = 0, rp1b = 0;
-
-#define A_LD(j) if constexpr (j < S::A_PER_T) { if (a_on##j) ra##j = *(const uint4*)(a_src##j + _o); }
-#define SK_LOAD_A(kt)                                                          \
-  do {                                                                         \
-    const int64_t _o = (int64_t)(kt) * kBK;                                    \
-    FLEXQ_SK_FOR8(A_LD)                                                        \
-  } while (0)
-#define A_ST(j) if constexpr (j < S::A_PER_T) { if (a_on##j) *(uint4*)(_a + a_lds##j) = ra##j; }
-#define SK_STORE_A(buf)                                                        \
-  do {                                                                         \
-    f16* _a = smem + (buf) * kStageA;                                          \
-    FLEXQ_SK_FOR8(A_ST)                                                        \
-  } while (0)
-#define SK_LOAD_B(kt, SET)                                                     \
-  do {                                                                         \
-    const int64_t _kt = (kt);                                                  \
-    rb0##SET = *(const uint4*)(b_src0 + _kt * 32);                             \
-    rp0##SET = p_src0[_kt];                                                    \
-    if constexpr (TN > 1) {                                                    \
-      rb1##SET = *(const uint4*)(b_src1 + _kt * 32);                           \
-      rp1##SET = p_src1[_kt];                                                  \
-    }                                                                          \
-  } while (0)
+  // W row n0 + (2 w + j) 32 + l % 32, and that row's (offset, scale) word.
+  const int b_n0 = n0 + wave * 64 + (lane & 31), b_n1 = b_n0 + 32;
+  const int b_g0 = b_n0 < N ? b_n0 : 0, b_g1 = b_n1 < N ? b_n1 : 0;
+  const uint8_t* const b_src0 = Wc + (int64_t)b_g0 * ldc + g * 16;
+  const uint8_t* const b_src1 = Wc + (int64_t)b_g1 * ldc + g * 16;
+  const uint32_t* const p_src0 = Wp + (int64_t)b_g0 * ldp;
+  const uint32_t* const p_src1 = Wp + (int64_t)b_g1 * ldp;
+  // W codes of four k-tiles in flight: set = (k-tile - kt0) mod 4
+  uint4 rb0_0, rb1_0, rb0_1, rb1_1, rb0_2, rb1_2, rb0_3, rb1_3;
+  uint32_t rp0_0, rp1_0, rp0_1, rp1_1, rp0_2, rp1_2, rp0_3, rp1_3;
+  uint32_t dq_t0, dq_t1;
+  f16x2 dq_s0, dq_m0, dq_s1, dq_m1;
 
   f32x16 acc[MT][TN];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){0};
+  f16x8 fa0[MT], fb0[TN], fa1[MT], fb1[TN];
+  // A fragment of row slice i, k-step ks: LDS chunk 4 g + ks of row 32 i + (l & 31)
+  const int fa_base = (lane & 31) * 64;
+  const int f_sw = ((lane & 31) >> 1) & 7;
 
-  // one k-tile of MFMAs from LDS stage `buf` and B codes in set SET
-#define SK_COMPUTE(buf, SET)                                                              \
-  do {                                                                                    \
-    const f16* _a = smem + (buf) * kStageA;                                               \
-    const f16x2 _m0 = h2_from_u32((rp0##SET & 0xFFFFu) * 0x10001u);                       \
-    const f16x2 _s0 = h2_from_u32((rp0##SET >> 16) * 0x10001u);                           \
-    const f16x2 _m1 = h2_from_u32((rp1##SET & 0xFFFFu) * 0x10001u);                       \
-    const f16x2 _s1 = h2_from_u32((rp1##SET >> 16) * 0x10001u);                           \
-    const uint32_t _w0[4] = {rb0##SET.x, rb0##SET.y, rb0##SET.z, rb0##SET.w};             \
-    const uint32_t _w1[4] = {rb1##SET.x, rb1##SET.y, rb1##SET.z, rb1##SET.w};             \
-    _Pragma("unroll") for (int _ks = 0; _ks < 4; ++_ks) {                                 \
-      f16x8 _fb[TN];                                                                      \
-      {                                                                                   \
-        f16x2 _pr[4];                                                                     \
-        codes_to_pairs(_w0[_ks], _pr);                                                    \
-        _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
-          const f16x2 _d = dequant_pair(_pr[_e], _s0, _m0);                               \
-          _fb[0][2 * _e] = _d.x;                                                          \
-          _fb[0][2 * _e + 1] = _d.y;                                                      \
-        }                                                                                 \
-      }                                                                                   \
-      if constexpr (TN > 1) {                                                             \
-        f16x2 _pr[4];                                                                     \
-        codes_to_pairs(_w1[_ks], _pr);                                                    \
-        _Pragma("unroll") for (int _e = 0; _e < 4; ++_e) {                                \
-          const f16x2 _d = dequant_pair(_pr[_e], _s1, _m1);                               \
-          _fb[TN - 1][2 * _e] = _d.x;                                                     \
-          _fb[TN - 1][2 * _e + 1] = _d.y;                                                 \
-        }                                                                                 \
-      }                                                                                   \
-      _Pragma("unroll") for (int _i = 0; _i < MT; ++_i) {                                 \
-        const f16x8 _fa = *(const f16x8*)(_a + lds_off(_i * 32 + (lane & 31), 4 * g + _ks)); \
-        _Pragma("unroll") for (int _j = 0; _j < TN; ++_j)                                 \
-            acc[_i][_j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(_fa, _fb[_j], acc[_i][_j], 0, 0, 0); \
-      }                                                                                   \
-    }                                                                                     \
+#define SB() __builtin_amdgcn_sched_barrier(0)
+#define FRAG_A(F, BUF, KS, i) \
+  F[i] = *(const f16x8*)(smem + (BUF) * kStageA + fa_base + (i) * 32 * 64 + (((4 * g + (KS)) ^ f_sw) << 3))
+#define LOAD_A(j, SET, KT) \
+  if constexpr ((j) < MT) ra##SET##_##j = *(const uint4*)(a_src##j + (int64_t)(KT) * kBK)
+#define STORE_A(j, BUF) \
+  if constexpr ((j) < MT) *(uint4*)(smem + (BUF) * kStageA + a_lds + 32 * 64 * (j)) = ra##BUF##_##j
+#define LOAD_B(SET, KT)                                       \
+  do {                                                        \
+    rb0_##SET = *(const uint4*)(b_src0 + (int64_t)(KT) * 32); \
+    rb1_##SET = *(const uint4*)(b_src1 + (int64_t)(KT) * 32); \
+    rp0_##SET = p_src0[KT];                                   \
+    rp1_##SET = p_src1[KT];                                   \
+  } while (0)
+#define DQ_SCALE(SET)                                         \
+  do {                                                        \
+    dq_s0 = h2_from_u32((rp0_##SET >> 16) * 0x10001u);        \
+    dq_m0 = h2_from_u32((rp0_##SET & 0xFFFFu) * 0x10001u);    \
+    dq_s1 = h2_from_u32((rp1_##SET >> 16) * 0x10001u);        \
+    dq_m1 = h2_from_u32((rp1_##SET & 0xFFFFu) * 0x10001u);    \
+  } while (0)
+#define DQ_PRE(W) codes_to_bytes((W), dq_t0, dq_t1)
+// elements 2p, 2p + 1 of B fragment F[j]
+#define DQ_PAIR(F, j, p)                                                                   \
+  do {                                                                                     \
+    const f16x2 _d =                                                                       \
+        dequant_pair(code_pair_f16<(p) & 1>((p) < 2 ? dq_t0 : dq_t1), dq_s##j, dq_m##j);   \
+    F[j][2 * (p)] = _d[0];                                                                 \
+    F[j][2 * (p) + 1] = _d[1];                                                             \
+  } while (0)
+#define MF(FA, FB, e) \
+  acc[(e) / TN][(e) % TN] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FA[(e) / TN], FB[(e) % TN], acc[(e) / TN][(e) % TN], 0, 0, 0)
+// dequant item q (0..7) of the next k-step goes after MFMA slot q * NS / 8
+#define DQ_AT(e, q) ((e) == ((q) * NS) / 8)
+
+// One k-step region: the NS MFMAs of fragment set (FA, FB), each followed by a pinned
+// slice of side work: the next k-step's A fragments (set NA, stage BUF, k-step KS)
+// and B fragments (set NB, dequantized from word WORD of code set SET), A chunks of
+// k-tile kt+1 stored from register set NBUF to stage NBUF and that set reloaded with
+// k-tile kt+3 (chunk R, and R + 4 in region 0); region 0 also takes the scales of
+// k-tile kt and loads the codes of kt+3 into set LSET.
+#define REGION(FA, FB, NA, NB, BUF, KS, R, WORD, NBUF, SET, LSET, K3)     \
+  do {                                                                   \
+    _Pragma("unroll") for (int _e = 0; _e < NS; ++_e) {                  \
+      MF(FA, FB, _e);                                                    \
+      SB();                                                              \
+      if (_e < MT) FRAG_A(NA, BUF, KS, _e);                              \
+      if (_e == 0 && (R) == 0) { DQ_SCALE(SET); LOAD_B(LSET, K3); }      \
+      if (DQ_AT(_e, 0)) { DQ_PRE(rb0_##SET.WORD); DQ_PAIR(NB, 0, 0); }   \
+      if (DQ_AT(_e, 1)) DQ_PAIR(NB, 0, 1);                               \
+      if (DQ_AT(_e, 2)) DQ_PAIR(NB, 0, 2);                               \
+      if (DQ_AT(_e, 3)) DQ_PAIR(NB, 0, 3);                               \
+      if (DQ_AT(_e, 4)) { DQ_PRE(rb1_##SET.WORD); DQ_PAIR(NB, 1, 0); }   \
+      if (DQ_AT(_e, 5)) DQ_PAIR(NB, 1, 1);                               \
+      if (DQ_AT(_e, 6)) DQ_PAIR(NB, 1, 2);                               \
+      if (DQ_AT(_e, 7)) DQ_PAIR(NB, 1, 3);                               \
+      if (_e == NS - 1) {                                                \
+        STORE_A(R, NBUF); LOAD_A(R, NBUF, K3);                           \
+        if ((R) == 0) { STORE_A(4, NBUF); LOAD_A(4, NBUF, K3); }         \
+      }                                                                  \
+      SB();                                                              \
+    }                                                                    \
+  } while (0)
+#define TILE(BUF, NBUF, SET, LSET, KT)                                                  \
+  do {                                                                                  \
+    const int _k3 = min((KT) + 3, klast);                                               \
+    REGION(fa1, fb1, fa0, fb0, BUF, 0, 0, x, NBUF, SET, LSET, _k3);                     \
+    REGION(fa0, fb0, fa1, fb1, BUF, 1, 1, y, NBUF, SET, LSET, _k3);                     \
+    REGION(fa1, fb1, fa0, fb0, BUF, 2, 2, z, NBUF, SET, LSET, _k3);                     \
+    REGION(fa0, fb0, fa1, fb1, BUF, 3, 3, w, NBUF, SET, LSET, _k3);                     \
+    __syncthreads();                                                                    \
   } while (0)
 
-  // Branch-free pipeline (tile indices clamped to the last k-tile): A is one k-tile
-  // ahead in registers and LDS, B two k-tiles ahead in two register sets.  The loop
-  // body covers two k-tiles so that the register sets keep fixed names.
+  // Pipeline over k-tiles (indices clamped to the last k-tile, so every load and
+  // store is unconditional): while k-tile kt is multiplied out of LDS stage
+  // (kt - kt0) & 1 and code set (kt - kt0) & 3, A of kt+1 is written to the other
+  // stage, A and the codes of kt+3 are loaded: about 60 KB per CU in flight, enough to
+  // cover HBM latency with one block per CU (vector-memory waits count loads in issue
+  // order, so A and W must both be this far ahead).  The k-steps are rotated by one
+  // (region 0 finishes the previous k-tile; all-zero fragments before the first), and
+  // the loop is unrolled by four so that stages and code sets have fixed names.
   if (kt0 < kt1) {
     const int klast = kt1 - 1;
-    SK_LOAD_A(kt0);
-    SK_LOAD_B(kt0, a);
-    SK_LOAD_B(min(kt0 + 1, klast), b);
-    SK_STORE_A(0);
-    SK_LOAD_A(min(kt0 + 1, klast));
+    const int k1 = min(kt0 + 1, klast);
+    const int k2 = min(kt0 + 2, klast);
+    LOAD_A(0, 0, kt0); LOAD_A(1, 0, kt0); LOAD_A(2, 0, kt0); LOAD_A(3, 0, kt0); LOAD_A(4, 0, kt0);
+    LOAD_B(0, kt0);
+    LOAD_A(0, 1, k1); LOAD_A(1, 1, k1); LOAD_A(2, 1, k1); LOAD_A(3, 1, k1); LOAD_A(4, 1, k1);
+    LOAD_B(1, k1);
+    LOAD_B(2, k2);
+    STORE_A(0, 0); STORE_A(1, 0); STORE_A(2, 0); STORE_A(3, 0); STORE_A(4, 0);
+    LOAD_A(0, 0, k2); LOAD_A(1, 0, k2); LOAD_A(2, 0, k2); LOAD_A(3, 0, k2); LOAD_A(4, 0, k2);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) fa1[i] = (f16x8){0};
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb1[j] = (f16x8){0};
     __syncthreads();
     int kt = kt0;
-    for (; kt + 1 < kt1; kt += 2) {
-      // k-tile kt: LDS stage 0, B set a
-      SK_STORE_A(1);
-      SK_LOAD_A(min(kt + 2, klast));
-      SK_COMPUTE(0, a);
-      SK_LOAD_B(min(kt + 2, klast), a);
-      __syncthreads();
-      // k-tile kt + 1: LDS stage 1, B set b
-      SK_STORE_A(0);
-      SK_LOAD_A(min(kt + 3, klast));
-      SK_COMPUTE(1, b);
-      SK_LOAD_B(min(kt + 3, klast), b);
-      __syncthreads();
+    for (; kt + 3 < kt1; kt += 4) {
+      TILE(0, 1, 0, 3, kt);
+      TILE(1, 0, 1, 0, kt + 1);
+      TILE(0, 1, 2, 1, kt + 2);
+      TILE(1, 0, 3, 2, kt + 3);
     }
-    if (kt < kt1) SK_COMPUTE(0, a);
+    if (kt < kt1) TILE(0, 1, 0, 3, kt);
+    if (kt + 1 < kt1) TILE(1, 0, 1, 0, kt + 1);
+    if (kt + 2 < kt1) TILE(0, 1, 2, 1, kt + 2);
+#pragma unroll
+    for (int e = 0; e < NS; ++e) MF(fa1, fb1, e);
   }
-#undef SK_COMPUTE
-#undef SK_LOAD_B
-#undef SK_STORE_A
-#undef SK_LOAD_A
-#undef A_ST
-#undef A_LD
-#undef FLEXQ_SK_FOR8
-#undef FLEXQ_SK_FOR2
+#undef SB
+#undef FRAG_A
+#undef LOAD_A
+#undef STORE_A
+#undef LOAD_B
+#undef DQ_SCALE
+#undef DQ_PRE
+#undef DQ_PAIR
+#undef MF
+#undef DQ_AT
+#undef REGION
+#undef TILE
 
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
