@@ -58,6 +58,55 @@ __device__ __forceinline__ float epilogue_value(float v, const Epilogue& ep, int
   return v;
 }
 
+// Store one 32 x 32 MFMA accumulator tile: lane l holds column `col` and rows
+// row0 + 8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15.  Tiles whose rows all lie below M
+// take a branch-free path, so the bias and the 16 residual loads are issued together
+// instead of one dependent load per element.
+template <int OUT>
+__device__ __forceinline__ void store_acc_tile(const f32x16& a, int row0, int col, int M, int N,
+                                               const Epilogue& ep, void* __restrict__ Y,
+                                               int split) {
+  const int rl = row0 + 4 * ((threadIdx.x & 63) >> 5);
+  if (row0 + 32 <= M) {
+    if (col >= N) return;
+    if constexpr (OUT == kOutF16) {
+      const float b = ep.bias ? (float)ep.bias[col] : 0.0f;
+      float res[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) res[r] = 0.0f;
+      if (ep.residual) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          res[r] = (float)ep.residual[(int64_t)(rl + 8 * (r >> 2) + (r & 3)) * N + col];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = a[r] + b;
+        if (ep.relu) v = fmaxf(v, 0.0f);
+        v += res[r];
+        ((f16*)Y)[(int64_t)(rl + 8 * (r >> 2) + (r & 3)) * N + col] = (f16)v;
+      }
+    } else {
+      float* const y = (float*)Y + (OUT == kOutPartial ? (int64_t)split * M * N : 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) y[(int64_t)(rl + 8 * (r >> 2) + (r & 3)) * N + col] = a[r];
+    }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = rl + 8 * (r >> 2) + (r & 3);
+    if (row < M && col < N) {
+      if constexpr (OUT == kOutF16) {
+        ((f16*)Y)[(int64_t)row * N + col] = (f16)epilogue_value(a[r], ep, row, col, N);
+      } else {
+        float* const y = (float*)Y + (OUT == kOutPartial ? (int64_t)split * M * N : 0);
+        y[(int64_t)row * N + col] = a[r];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ large-M kernel
 //
 // Prefill shapes (M = 48 x 512 rows) use a 256 x 256 x 64 tile with 8 waves
@@ -286,26 +335,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
 #undef TILE
 
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * TN * 32 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * TM * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M && col < N) {
-          const float v = acc[i][j][r];
-          if constexpr (OUT == kOutF16) {
-            ((f16*)Y)[(int64_t)row * N + col] = (f16)epilogue_value(v, ep, row, col, N);
-          } else if constexpr (OUT == kOutF32) {
-            ((float*)Y)[(int64_t)row * N + col] = v;
-          } else {
-            ((float*)Y)[((int64_t)blockIdx.y * M + row) * N + col] = v;
-          }
-        }
-      }
-    }
-  }
+    for (int j = 0; j < TN; ++j)
+      store_acc_tile<OUT>(acc[i][j], m0 + wm * TM * 32 + i * 32,
+                          n0 + wn * TN * 32 + j * 32 + (lane & 31), M, N, ep, Y, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ small-M kernel
@@ -510,26 +544,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
 #undef TILE
 
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + (wave * TN + j) * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M && col < N) {
-          const float v = acc[i][j][r];
-          if constexpr (OUT == kOutF16) {
-            ((f16*)Y)[(int64_t)row * N + col] = (f16)epilogue_value(v, ep, row, col, N);
-          } else if constexpr (OUT == kOutF32) {
-            ((float*)Y)[(int64_t)row * N + col] = v;
-          } else {
-            ((float*)Y)[((int64_t)blockIdx.y * M + row) * N + col] = v;
-          }
-        }
-      }
-    }
-  }
+    for (int j = 0; j < TN; ++j)
+      store_acc_tile<OUT>(acc[i][j], m0 + i * 32, n0 + (wave * TN + j) * 32 + (lane & 31), M, N,
+                          ep, Y, blockIdx.y);
 }
 
 // Sum of split-K partials in split order, then the epilogue.  4 elements per thread.
