@@ -35,7 +35,7 @@ constexpr int kDecMaxChunk = 4096;  // tokens of one split (scores live in LDS)
 template <int N>
 __device__ __forceinline__ float byte_f(uint32_t w) { return (float)((w >> (8 * N)) & 0xFFu); }
 
-template <int HD>
+template <int HD, int UNR>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict__ qkv, int b0,
                                                           int pos, KVViewD kv, int chunk,
                                                           f16* __restrict__ out,
@@ -103,14 +103,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     }
   }
 
-  // ---- 2. K pass
-  for (int tb = t_begin; tb < t_end; tb += TPB) {
-    const int t = tb + wave * TPW + lane / LPT;
-    float partial = 0.0f;
-    if (t < t_end) {
-      const uint4 cw = *(const uint4*)(kv.kc + (slot0 + t) * (HD / 2) + 16 * j);
-      const uint32_t prm = kv.kp[(slot0 + t) * GPT + grp];
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  // ---- 2. K pass, UNR block steps per iteration: every load of the iteration is
+  // issued before the first use (token index clamped to the split's last token, the
+  // results of clamped lanes discarded), so UNR x 20 B per lane are in flight
+  for (int tb = t_begin; tb < t_end; tb += UNR * TPB) {
+    uint4 cw[UNR];
+    uint32_t prm[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
+      cw[u] = *(const uint4*)(kv.kc + (slot0 + t) * (HD / 2) + 16 * j);
+      prm[u] = kv.kp[(slot0 + t) * GPT + grp];
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = tb + u * TPB + wave * TPW + lane / LPT;
+      const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
       float dot = 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -121,13 +129,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
         dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c060c02u)), q2[4 * k + 2], dot, false);
         dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c070c03u)), q2[4 * k + 3], dot, false);
       }
-      const float m = (float)h_from_bits(prm & 0xFFFFu);
-      const float s = (float)h_from_bits(prm >> 16);
-      partial = (s * 16777216.0f) * dot + m * qsum;
-    }
+      const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
+      const float s = (float)h_from_bits(prm[u] >> 16);
+      float partial = (s * 16777216.0f) * dot + m * qsum;
 #pragma unroll
-    for (int o = 1; o < LPT; o <<= 1) partial += __shfl_xor(partial, o, 64);
-    if (j == 0 && t < t_end) sc[t - t_begin] = partial * scale_log2;
+      for (int o = 1; o < LPT; o <<= 1) partial += __shfl_xor(partial, o, 64);
+      if (j == 0 && t < t_end) sc[t - t_begin] = partial * scale_log2;
+    }
   }
   __syncthreads();
 
@@ -156,17 +164,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float pm = 0.0f;
-  for (int tb = t_begin; tb < t_end; tb += TPB) {
-    const int t = tb + wave * TPW + lane / LPT;
-    if (t < t_end) {
-      const float p = sc[t - t_begin];
-      const uint4 cw = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
-      const uint32_t prm = kv.vp[(slot0 + t) * GPT + grp];
-      const float m = (float)h_from_bits(prm & 0xFFFFu);
-      const float s = (float)h_from_bits(prm >> 16);
+  for (int tb = t_begin; tb < t_end; tb += UNR * TPB) {
+    uint4 cw[UNR];
+    uint32_t prm[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
+      cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
+      prm[u] = kv.vp[(slot0 + t) * GPT + grp];
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = tb + u * TPB + wave * TPW + lane / LPT;
+      // clamped lanes repeat the last token: their weight is zero
+      const float p = t < t_end ? sc[t - t_begin] : 0.0f;
+      const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
+      const float s = (float)h_from_bits(prm[u] >> 16);
       const float ps = p * s;
       pm += p * m;
-      const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+      const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
@@ -232,8 +248,16 @@ __global__ __launch_bounds__(HD) void attn_decode_merge_kernel(const float* __re
 }
 
 struct DecPlan {
-  int splits, chunk;
+  int splits, chunk, unr;
 };
+
+// Unroll of the token loops: the largest of 4, 3, 2 that wastes at most 1/8 of the
+// block steps of a split on clamped lanes, else 1.
+static int dec_unroll(int steps) {
+  for (int u = 4; u >= 2; --u)
+    if (((steps + u - 1) / u * u - steps) * 8 <= steps) return u;
+  return 1;
+}
 
 static DecPlan dec_plan(int B, int heads, int head_dim, int pos) {
   const int T = pos + 1;
@@ -245,8 +269,30 @@ static DecPlan dec_plan(int B, int heads, int head_dim, int pos) {
   int chunk = (T + splits - 1) / splits;
   chunk = (chunk + step - 1) / step * step;
   if (chunk > kDecMaxChunk) chunk = kDecMaxChunk;
-  DecPlan p{(T + chunk - 1) / chunk, chunk};
+  const int nsplit = (T + chunk - 1) / chunk;
+  // the longest split decides; shorter (last) splits only clamp more lanes
+  DecPlan p{nsplit, chunk, dec_unroll((std::min(chunk, T) + step - 1) / step)};
   return p;
+}
+
+template <int HD, int UNR>
+static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
+                       const KVViewD& v, f16* out, float* ws, float scale_log2,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL((attn_decode_kernel<HD, UNR>), grid, dim3(256), 0, stream, qkv, b0, pos, v,
+                     p.chunk, out, ws, scale_log2);
+}
+
+template <int HD>
+static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
+                       const KVViewD& v, f16* out, float* ws, float scale_log2,
+                       hipStream_t stream) {
+  switch (p.unr) {
+    case 4: launch_dec<HD, 4>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
+    case 3: launch_dec<HD, 3>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
+    case 2: launch_dec<HD, 2>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
+    default: launch_dec<HD, 1>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
+  }
 }
 
 }  // namespace flexq
@@ -282,14 +328,12 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
   dim3 grid(p.splits, kv->heads, B);
   if (kv->head_dim == 64) {
-    hipLaunchKernelGGL(attn_decode_kernel<64>, grid, dim3(256), 0, stream, (const f16*)qkv, b0, pos,
-                       v, p.chunk, (f16*)out, (float*)ws, scale_log2);
+    launch_dec<64>(p, grid, (const f16*)qkv, b0, pos, v, (f16*)out, (float*)ws, scale_log2, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(kv->heads, B), dim3(64), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);
   } else {
-    hipLaunchKernelGGL(attn_decode_kernel<128>, grid, dim3(256), 0, stream, (const f16*)qkv, b0,
-                       pos, v, p.chunk, (f16*)out, (float*)ws, scale_log2);
+    launch_dec<128>(p, grid, (const f16*)qkv, b0, pos, v, (f16*)out, (float*)ws, scale_log2, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(kv->heads, B), dim3(128), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);
