@@ -2,15 +2,26 @@
 // the 4-bit KV store fused at the end (walkthrough section 6.3, cache config:
 // group 64 along head_dim).
 //
-// One work-group per (64-query block, head, sequence); 4 waves of 16 queries.
-// Key/value blocks of 64 positions are staged in LDS (K row-major, V transposed),
-// scores come from v_mfma_f32_16x16x32_f16 as S^T = K . Q^T, an online softmax in
-// fp32 (exp2 with the 1/sqrt(hd) * log2(e) factor folded into the scores) keeps a
-// running max/sum per query, and O^T += V^T . P^T reuses the score registers
-// directly as the B operand: lane (q + 16 g) holds keys 4g..4g+3 of two 16-key
-// tiles, so both operands number the 32 keys of a step the same way.
-// After the softmax loop the group quantizes K and V of its own 64 positions into
-// the cache (8 lanes per 64-element group), reading them back from the qkv rows.
+// One work-group per (128-query block, head, sequence), two resident per CU; 4 waves
+// of 32 queries, one MFMA tile (v_mfma_f32_32x32x16_f16) wide.  Key blocks of 64 positions are staged
+// in LDS by 16-B copies (K rows XOR-swizzled, V rows padded), two stages deep: the
+// next block is loaded into registers while the current one is multiplied, one
+// barrier per block.
+//  * scores S^T = K . Q^T, 32 keys x 32 queries per tile: the K operand is read from
+//    LDS, Q^T stays in registers; lane l owns query l % 32 and 16 keys of each tile
+//    (rows 8 (r / 4) + 4 (l / 32) + r % 4), so a query's softmax statistics need
+//    one exchange with lane l ^ 32;
+//  * online softmax in fp32 (exp2 with 1/sqrt(hd) * log2(e) fused into its argument,
+//    lazy rescaling of the output when a query's running max grows by more than 8);
+//  * O^T += V^T . P^T, 16 keys per MFMA: the probabilities are used from the score
+//    registers as the B operand (register r of tile t is key 32 t + 16 (r / 8) +
+//    8 ((r / 4) % 2) + 4 (l / 32) + r % 4), and the matching V^T operand -- four
+//    consecutive keys of one dimension per lane, twice -- comes straight from the
+//    row-major V tile through the transposing LDS read ds_read_b64_tr_b16: within
+//    each 16-lane group, lane j points at 4 dims of key j / 4 and lane i receives
+//    dim i of the 4 keys.
+// After the loop the work-group quantizes K and V of its own 128 positions into the
+// cache (8 lanes per 64-element group), reading them from the staged LDS tiles.
 #include "quant_dev.h"
 
 namespace flexq {
@@ -23,149 +34,225 @@ struct KVView {
   int nh, max_len;
 };
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
 template <int HD>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const f16* __restrict__ qkv, int S,
+struct PrefillShape {
+  static constexpr int QB = 128;                 // queries per work-group
+  static constexpr int KB = 64;                  // keys per block step
+  static constexpr int HC = HD / 8;              // 16-B chunks per K/V row
+  static constexpr int VLD = HD + 32;            // padded V row (halves): rows 4 apart
+                                                 // in LDS banks for the transposing read
+  static constexpr int K_STAGE = KB * HD;        // halves
+  static constexpr int V_STAGE = KB * VLD;       // halves
+  static constexpr int CH_PER_T = KB * HC / 256; // 16-B chunks of K (and of V) per thread
+  static constexpr size_t LDS_BYTES = 2 * (size_t)(K_STAGE + V_STAGE) * sizeof(f16);
+};
+
+// swizzled position of 16-B chunk `ch` in K row `row` (conflict-free b128 reads of
+// 32 consecutive rows at one chunk)
+template <int HD>
+__device__ __forceinline__ int k_off(int row, int ch) {
+  if constexpr (HD == 128) return row * HD + ((ch ^ (row & 15)) << 3);
+  else return row * HD + ((ch ^ ((row >> 1) & 7)) << 3);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restrict__ qkv, int S,
                                                            int nh, int b0, KVView kv,
                                                            f16* __restrict__ out,
                                                            float scale_log2) {
-  constexpr int KB = 64;           // keys per block
-  constexpr int HC = HD / 8;       // 16-B chunks per K row
-  constexpr int VT_LD = KB + 8;    // transposed V row length (halves)
-  __shared__ __attribute__((aligned(16))) f16 sK[KB * HD];
-  __shared__ __attribute__((aligned(16))) f16 sVt[HD * VT_LD];
+  using P = PrefillShape<HD>;
+  constexpr int QB = P::QB, KB = P::KB, HC = P::HC, VLD = P::VLD;
+  constexpr int KS = HD / 16;        // k-steps of a score tile
+  constexpr int DT = HD / 32;        // output dim tiles
+  constexpr int CPT = P::CH_PER_T;
+  extern __shared__ __attribute__((aligned(16))) f16 smem[];
+  f16* const sK = smem;                          // [2][KB * HD]
+  f16* const sV = smem + 2 * P::K_STAGE;         // [2][KB * VLD]
 
-  const int nqb = (S + 63) / 64;
-  const int qb = nqb - 1 - blockIdx.x;  // long (late) query blocks first
-  const int head = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1-D grid of (query block, head, sequence) items.  The dispatcher deals work-groups
+  // to the 8 XCDs round-robin; item order is remapped so that each XCD runs a
+  // contiguous range, in which the query blocks of one (sequence, head) -- which
+  // stage the same K/V rows -- follow each other and share that XCD's L2.  Long
+  // (late) query blocks come first within each (sequence, head).
+  const int nqb = (S + QB - 1) / QB;
+  const int items = (int)gridDim.x;
+  int w = blockIdx.x;
+  if (items % 8 == 0) w = (w & 7) * (items >> 3) + (w >> 3);
+  const int qb = nqb - 1 - w % nqb;
+  const int head = (w / nqb) % nh;
+  const int b = w / (nqb * nh);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = nh * HD;
   const int64_t ld = 3 * (int64_t)h;
   const f16* base = qkv + (int64_t)b * S * ld;
-  const int q0 = qb * 64;
-  const int g = lane >> 4;           // lane group 0..3
-  const int ql = lane & 15;          // query within the wave's 16
-  const int qabs = q0 + wave * 16 + ql;
+  const int q0 = qb * QB;
+  const int wq0 = q0 + wave * 32;          // first query of this wave
+  const int hl = lane >> 5;                // lane half
+  const int qabs = wq0 + (lane & 31);
   const int qrow = min(qabs, S - 1);
+  const int kend = min(q0 + QB, S);        // keys this work-group needs: [0, kend)
+  const int nkb = (kend + KB - 1) / KB;
 
-  // Q^T operand: lane (q + 16g) holds Q[q][32 ks + 8 g .. +7]
-  f16x8 qf[HD / 32];
+  // Q^T operand: lane (q, half) holds Q[q][16 ks + 8 half .. +7]
+  f16x8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < HD / 32; ++ks)
-    qf[ks] = *(const f16x8*)(base + (int64_t)qrow * ld + head * HD + ks * 32 + g * 8);
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = *(const f16x8*)(base + (int64_t)qrow * ld + head * HD + 16 * ks + 8 * hl);
 
-  f32x4 o[HD / 16];
+  f32x16 o[DT];
 #pragma unroll
-  for (int i = 0; i < HD / 16; ++i) o[i] = (f32x4){0, 0, 0, 0};
+  for (int i = 0; i < DT; ++i) o[i] = (f32x16){0};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  for (int kb = 0; kb <= qb; ++kb) {
+  // staging: thread t copies chunks c = t + 256 u of the block's K and V rows
+  // (row c / HC, chunk c % HC); keys past S read row S - 1 and are masked.  The
+  // registers are named scalars (arrays of them would live in scratch memory).
+  static_assert(CPT == 2 || CPT == 4, "staging copies are stamped out for 2 or 4 per thread");
+  uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
+#define PF_LD(u, KB_)                                                           \
+  if constexpr ((u) < CPT) {                                                    \
+    const int _c = tid + 256 * (u);                                             \
+    const int _key = min((KB_) * KB + _c / HC, S - 1);                          \
+    const f16* _row = base + (int64_t)_key * ld + head * HD + (_c % HC) * 8;    \
+    rk##u = *(const uint4*)(_row + h);                                          \
+    rv##u = *(const uint4*)(_row + 2 * h);                                      \
+  }
+#define PF_ST(u, ST_)                                                           \
+  if constexpr ((u) < CPT) {                                                    \
+    const int _c = tid + 256 * (u);                                             \
+    const int _r = _c / HC, _ch = _c % HC;                                      \
+    *(uint4*)(sK + (ST_) * P::K_STAGE + k_off<HD>(_r, _ch)) = rk##u;            \
+    *(uint4*)(sV + (ST_) * P::V_STAGE + _r * VLD + _ch * 8) = rv##u;            \
+  }
+#define LOAD_KV(KB_) do { PF_LD(0, KB_) PF_LD(1, KB_) PF_LD(2, KB_) PF_LD(3, KB_) } while (0)
+#define STORE_KV(ST_) do { PF_ST(0, ST_) PF_ST(1, ST_) PF_ST(2, ST_) PF_ST(3, ST_) } while (0)
+
+  // transposing-read lane geometry: 16-lane group a = lane / 16 covers dims
+  // 16 (a % 2) .. +15 of a 32-dim tile and keys 4 (a / 2) .. +3 (+8) of a 16-key step
+  const int tr_i = lane & 15;
+  const int tr_key = 4 * hl + (tr_i >> 2);
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
+
+  LOAD_KV(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    STORE_KV(st);
+    if (kb + 1 < nkb) LOAD_KV(kb + 1);
+    __syncthreads();
     const int k0 = kb * KB;
-    __syncthreads();
-    // stage K rows (swizzled 16-B chunks) and V transposed
-    for (int idx = tid; idx < KB * HC; idx += 256) {
-      const int key = idx / HC, ch = idx % HC;
-      const int t = k0 + key;
-      uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = make_uint4(0, 0, 0, 0);
-      if (t < S) {
-        const f16* row = base + (int64_t)t * ld + head * HD + ch * 8;
-        kv4 = *(const uint4*)(row + h);
-        vv4 = *(const uint4*)(row + 2 * h);
-      }
-      *(uint4*)(sK + key * HD + ((ch ^ (key & 7)) << 3)) = kv4;
-      const f16x8 vh = __builtin_bit_cast(f16x8, vv4);
+    if (k0 <= wq0 + 31) {   // some key of the block is visible to some query of the wave
+      const f16* sk = sK + st * P::K_STAGE;
+      const f16* sv = sV + st * P::V_STAGE;
+      f32x16 s[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(ch * 8 + e) * VT_LD + key] = vh[e];
-    }
-    __syncthreads();
-
-    // S^T tiles: 4 tiles of 16 keys; lane (q + 16g) reg r = key 16 t + 4 g + r
-    f32x4 s[4];
+      for (int t = 0; t < 2; ++t) {
+        s[t] = (f32x16){0};
+        const int krow = 32 * t + (lane & 31);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      s[t] = (f32x4){0, 0, 0, 0};
-      const int krow = t * 16 + ql;
-#pragma unroll
-      for (int ks = 0; ks < HD / 32; ++ks) {
-        const int ch = ks * 4 + g;
-        const f16x8 kf = *(const f16x8*)(sK + krow * HD + ((ch ^ (krow & 7)) << 3));
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s[t], 0, 0, 0);
-      }
-    }
-    // scale, mask (causal and past the end), block max
-    const bool diag = (kb == qb) || (k0 + KB > S);
-    float mb = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = s[t][r] * scale_log2;
-        if (diag) {
-          const int key = k0 + t * 16 + g * 4 + r;
-          if (key > qabs || key >= S) v = -INFINITY;
+        for (int ks = 0; ks < KS; ++ks) {
+          const f16x8 kf = *(const f16x8*)(sk + k_off<HD>(krow, 2 * ks + hl));
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], s[t], 0, 0, 0);
         }
-        s[t][r] = v;
-        mb = fmaxf(mb, v);
       }
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = exp2f(m_run - m_new);  // m_run = -inf on the first block -> 0
-    float ls = 0.0f;
-    f16x8 pf[2];
+      // mask (causal and past the end) and block max on the raw scores (the scale is
+      // positive, so it commutes with the max).  Register r of tile t is key
+      // k0 + 32 t + 8 (r / 4) + 4 (l / 32) + r % 4: one compare of its constant offset
+      // against a per-lane limit.
+      if ((k0 + KB - 1 > wq0) || (k0 + KB > S)) {
+        const int lim = min(qabs, S - 1) - k0 - 4 * hl;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[t][r] - m_new);
-        ls += p;
-        pf[t >> 1][(t & 1) * 4 + r] = (f16)p;
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
       }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+      float mb = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < HD / 16; ++i) o[i] *= alpha;
-
-    // O^T[d][q] += sum over 32-key steps of V^T[d][key] P^T[key][q]
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[t][r]);
+      mb = fmaxf(mb, __shfl_xor(mb, 32, 64)) * scale_log2;
+      // Lazy rescaling: the reference point m_run only moves when the block max exceeds
+      // it by more than 8 (probabilities stay <= 2^8, far inside fp16's range and at
+      // the same relative precision); otherwise O and l keep their scale.
+      const bool grow = mb > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {   // wave-uniform branch
+        const float m_new = grow ? mb : m_run;
+        const float alpha = exp2f(m_run - m_new);  // m_run = -inf on the first block -> 0
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt) {
-        const f16* vrow = sVt + (dt * 16 + ql) * VT_LD + kc * 32 + g * 4;
-        const f16x4 lo = *(const f16x4*)(vrow);
-        const f16x4 hi = *(const f16x4*)(vrow + 16);
-        const f16x8 vf = (f16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[kc], o[dt], 0, 0, 0);
+        for (int i = 0; i < DT; ++i) o[i] *= alpha;
+        m_run = m_new;
+      }
+      float ls = 0.0f;
+      f16x8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // v_exp_f32: results below 2^-126 flush to 0 (they vanish in the fp16 P anyway)
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], scale_log2, -m_run));
+          ls += p;
+          pf[2 * t + (r >> 3)][r & 7] = (f16)p;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l_run += ls;
+      // O^T += V^T P^T over the four 16-key steps
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f16* vp = sv + (16 * ss + tr_key) * VLD + 32 * dt + tr_dim;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vp));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vp + 8 * VLD));
+          const f16x8 vf = __builtin_bit_cast(
+              f16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[ss], o[dt], 0, 0, 0);
+        }
       }
     }
   }
 
-  // O^T lane (q + 16 g) reg r = dim 16 dt + 4 g + r of query q
+#undef PF_LD
+#undef PF_ST
+#undef LOAD_KV
+#undef STORE_KV
+
+  // O^T lane l reg r = dim 32 dt + 8 (r / 4) + 4 (l / 32) + r % 4 of query l % 32
   if (qabs < S) {
     const float inv = 1.0f / l_run;
     f16* orow = out + ((int64_t)b * S + qabs) * h + head * HD;
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) {
-      const f16x4 v = (f16x4){(f16)(o[dt][0] * inv), (f16)(o[dt][1] * inv), (f16)(o[dt][2] * inv),
-                              (f16)(o[dt][3] * inv)};
-      *(f16x4*)(orow + dt * 16 + g * 4) = v;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x4 v = (f16x4){(f16)(o[dt][4 * j] * inv), (f16)(o[dt][4 * j + 1] * inv),
+                                (f16)(o[dt][4 * j + 2] * inv), (f16)(o[dt][4 * j + 3] * inv)};
+        *(f16x4*)(orow + 32 * dt + 8 * j + 4 * hl) = v;
+      }
   }
 
-  // 4-bit store of K and V for positions [q0, q0 + 64): 8 lanes per group
+  // 4-bit store of K and V for positions [q0, q0 + 128) from the staged tiles (key
+  // block 2 qb + i sits in stage i; the last block's stores preceded the last barrier)
   constexpr int GPT = HD / 64;                     // groups per token vector
-  constexpr int NGROUPS = 64 * GPT * 2;            // K and V
+  constexpr int NGROUPS = QB * GPT * 2;            // K and V
   const int sub = tid & 7;
   for (int gi = tid >> 3; gi < NGROUPS; gi += 32) {
-    const int isv = gi / (64 * GPT);
-    const int rem = gi % (64 * GPT);
-    const int tok = q0 + rem / GPT;
+    const int isv = gi / (QB * GPT);
+    const int rem = gi % (QB * GPT);
+    const int tr = rem / GPT;                      // position within the 128
     const int grp = rem % GPT;
-    const int tl = min(tok, S - 1);
-    const f16* src = base + (int64_t)tl * ld + (1 + isv) * h + head * HD + grp * 64 + sub * 8;
-    const f16x8 xv = *(const f16x8*)src;
+    const int tok = q0 + tr;
+    const int stg = tr / KB, row = tr % KB;
+    const int ch = grp * 8 + sub;
+    f16x8 xv;
+    if (isv) xv = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8);
+    else xv = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch));
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (float)xv[e];
@@ -200,13 +287,22 @@ extern "C" int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int
   KVView v{kv->k_codes, kv->v_codes, (uint32_t*)kv->k_params, (uint32_t*)kv->v_params, kv->heads,
            kv->max_len};
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
-  dim3 grid((S + 63) / 64, kv->heads, B);
+  const int64_t items = (int64_t)((S + 127) / 128) * kv->heads * B;
+  if (items > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)items);
+  static bool attr_set = false;   // 72 KB of LDS for head_dim 128: above the default limit
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<128>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)PrefillShape<128>::LDS_BYTES);
+    attr_set = true;
+  }
   if (kv->head_dim == 64)
-    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, stream, (const f16*)qkv, S,
-                       kv->heads, b0, v, (f16*)out, scale_log2);
+    hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), PrefillShape<64>::LDS_BYTES, stream,
+                       (const f16*)qkv, S, kv->heads, b0, v, (f16*)out, scale_log2);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), 0, stream, (const f16*)qkv, S,
-                       kv->heads, b0, v, (f16*)out, scale_log2);
+    hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), PrefillShape<128>::LDS_BYTES,
+                       stream, (const f16*)qkv, S, kv->heads, b0, v, (f16*)out, scale_log2);
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
 }

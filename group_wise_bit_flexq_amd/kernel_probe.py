@@ -6,6 +6,9 @@
     python -m group_wise_bit_flexq_amd.kernel_probe decode --workload opt175b --reps 2
         one decode step's 4-bit GEMMs (M = batch) and decode attention over a cache
         of prompt + gen/2 positions;
+    python -m group_wise_bit_flexq_amd.kernel_probe prefill_attn --workload opt175b --reps 3
+        causal prefill attention of one micro-batch (micro_batch x prompt tokens, all
+        heads) with the fused 4-bit KV store;
     python -m group_wise_bit_flexq_amd.kernel_probe quant --reps 3
         the standalone quantizer on a 4 GiB fp16 tensor [524288][4096];
     python -m group_wise_bit_flexq_amd.kernel_probe stress --reps 3
@@ -79,6 +82,20 @@ def decode(wl, reps):
     return res
 
 
+def prefill_attn(wl, reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    B, S, nh, hd = wl.micro_batch, wl.prompt, wl.heads, wl.head_dim
+    kv = F.KV4(B, nh, hd, S)
+    qkv = synth.normal_fp16((B * S, 3 * nh * hd), 1.0, 7, device="cuda")
+    out = torch.empty(B * S, nh * hd, dtype=torch.float16, device="cuda")
+    ms = _time(lambda: F.attn_prefill(qkv, B, S, kv, out=out), reps)
+    flop = B * nh * 2 * (2 * hd * S * (S + 1) / 2)      # QK^T and PV over the causal half
+    return {"B": B, "S": S, "heads": nh, "head_dim": hd, "ms": ms, "tflops": flop / ms / 1e9}
+
+
 def quant(reps):
     import torch
 
@@ -121,7 +138,7 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "quant", "stress", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "stress", "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -134,6 +151,8 @@ def main():
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
+    elif a.what == "prefill_attn":
+        r = prefill_attn(wl, a.reps)
     elif a.what == "quant":
         r = quant(a.reps)
     elif a.what == "stress":

@@ -163,7 +163,8 @@ def _make_qkv(rng, B, S, nh, hd):
 
 
 @pytest.mark.parametrize("B,S,nh,hd", [(1, 1, 1, 64), (2, 17, 3, 64), (2, 130, 2, 128),
-                                       (1, 64, 4, 128), (3, 200, 2, 64)])
+                                       (1, 64, 4, 128), (3, 200, 2, 64), (2, 300, 2, 128),
+                                       (1, 512, 3, 128), (2, 385, 2, 64)])
 def test_attn_prefill(B, S, nh, hd):
     F = require_gpu()
     _say("attn_prefill", B, S, nh, hd)
