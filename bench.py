@@ -142,8 +142,14 @@ def decode_bytes(wl):
 
 
 def gemm_source_hash():
-    p = os.path.join(ROOT, "group_wise_bit_flexq_amd", "csrc", "gemm_w4.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the device code the prefill GEMM is built from: common.h and gemm_w4.hip
+    up to its host-dispatch section (host-side planning changes do not invalidate
+    counters taken on the kernel)."""
+    csrc = os.path.join(ROOT, "group_wise_bit_flexq_amd", "csrc")
+    gemm = open(os.path.join(csrc, "gemm_w4.hip"), "rb").read()
+    cut = gemm.find(b"// ------------------------------------------------------------------ host dispatch")
+    body = open(os.path.join(csrc, "common.h"), "rb").read() + (gemm[:cut] if cut >= 0 else gemm)
+    return hashlib.sha256(body).hexdigest()[:16]
 
 
 def traffic_from_profiles(wl):

@@ -591,6 +591,41 @@ struct Plan {
 constexpr int kCfgBig = 0;      // M > 160: 256 x 256 tile, 8 waves (pipelined, dequant into LDS)
 constexpr int kCfgSkinny = 1;   // M <= 160: 32*ceil(M/32) x 256 tile, W streamed to registers
 
+// Work-groups of the small-M kernel that one device runs at once (occupancy x CUs),
+// cached per device and tile height.
+template <int MT>
+static int skinny_blocks_per_cu() {
+  static int n = 0;
+  if (n == 0) {
+    int b = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b, gemm_w4_skinny_kernel<MT, 4, 2, kOutPartial>, 256, SkinnyShape<MT, 4, 2>::LDS_BYTES);
+    n = b > 0 ? b : 1;
+  }
+  return n;
+}
+
+static int64_t skinny_concurrency(int mt) {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const int slot = dev >= 0 && dev < 64 ? dev : 0;
+  if (cus[slot] == 0) {
+    int n = 0;
+    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    cus[slot] = n > 0 ? n : 256;
+  }
+  int per_cu = 1;
+  switch (mt) {
+    case 1: per_cu = skinny_blocks_per_cu<1>(); break;
+    case 2: per_cu = skinny_blocks_per_cu<2>(); break;
+    case 3: per_cu = skinny_blocks_per_cu<3>(); break;
+    case 4: per_cu = skinny_blocks_per_cu<4>(); break;
+    default: per_cu = skinny_blocks_per_cu<5>(); break;
+  }
+  return (int64_t)per_cu * cus[slot];
+}
+
 static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   Plan p;
   if (M <= 160) { p.cfg = kCfgSkinny; p.bm = (int)((M + 31) / 32) * 32; p.bn = 256; }
@@ -598,14 +633,31 @@ static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   const int64_t KT = K / kBK;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int splits = 1;
-  // too few work-groups for 256 CUs: split K (a fixed rule, so results depend only on
-  // the shape and on whether the workspace is large enough)
-  if (tiles < 512) {
+  if (p.cfg == kCfgSkinny) {
+    // Split-K count of the small-M kernel from a cost model fitted on MI355X at the
+    // decode shapes: time ~ rounds of resident work-groups x (a fixed cost of ~16
+    // k-tiles per work-group + its k-tiles) + the partial sums written and reduced
+    // (~4.75 MB per k-tile time).  Rounds matter: 576 work-groups on 256 CUs cost as
+    // much as 768.
+    const int64_t conc = skinny_concurrency(p.bm / 32);
+    double best = 1e300;
+    for (int64_t s = 1; s <= 8 && s <= KT; ++s) {
+      const int64_t kps = (KT + s - 1) / s;
+      const int64_t sp = (KT + kps - 1) / kps;
+      const int64_t rounds = (tiles * sp + conc - 1) / conc;
+      double c = (double)rounds * (double)(16 + kps);
+      if (sp > 1) c += (double)sp * (double)M * (double)N * 4.0 / 4.75e6;
+      if (c < best) {
+        best = c;
+        splits = (int)sp;
+      }
+    }
+  } else if (tiles < 512) {
+    // too few work-groups for 256 CUs: split K (a fixed rule, so results depend only
+    // on the shape and on whether the workspace is large enough)
     splits = (int)((512 + tiles - 1) / tiles);
     splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, KT / 8));
-    // the small-M kernel streams W once; beyond 4 splits its partial sums cost more
-    // traffic than the extra work-groups win (measured on the OPT-175B decode shapes)
-    splits = std::min(splits, p.cfg == kCfgSkinny ? 4 : 16);
+    splits = std::min(splits, 16);
   }
   if ((M * N) % 4) splits = 1;
   while (splits > 1 && (size_t)splits * M * N * sizeof(float) > ws_bytes) --splits;
