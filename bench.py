@@ -91,7 +91,7 @@ def build_model(wl, seed, F, synth, workloads):
             torch.cuda.synchronize()
             log(f"built layer {l + 1}/{wl.layers} ({time.time() - t0:.1f}s)")
     emb16 = synth.model_tensor("embed", (wl.vocab, h), seed, dev)
-    emb = F.quantize(emb16)
+    emb = F.quantize_weight(emb16)
     del emb16
     pos = synth.model_tensor("pos", (workloads.POS_ROWS, h), seed, dev)
     lnf_g = synth.model_tensor("lnf_g", (h,), seed, dev)

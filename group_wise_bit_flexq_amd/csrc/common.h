@@ -13,10 +13,32 @@ typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw (stride 0) buffer resource over `bytes` bytes at p: loads at an offset past the end
+// return zeros.  Word 3 is the gfx9 default (32-bit data format, no swizzle).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 #define FLEXQ_WAVE 64
 
 namespace flexq {
+
+// 4-bit weight layout (flexq_w4): rows in blocks of 128; within a block, k-tile kt (64
+// columns = one quantization group per row) holds the block's 128 x 32 bytes of codes
+// contiguously (4 KiB), and its 128 (offset, scale) words contiguously, so a k-tile of
+// any run of rows is read in whole cache lines.
+constexpr int kW4BlockRows = 128;
+constexpr int kW4TileBytes = kW4BlockRows * 32;
+__host__ __device__ __forceinline__ int64_t w4_code_off(int64_t row, int64_t kt, int64_t KT) {
+  return ((row >> 7) * KT + kt) * kW4TileBytes + (row & 127) * 32;   // bytes
+}
+__host__ __device__ __forceinline__ int64_t w4_param_idx(int64_t row, int64_t kt, int64_t KT) {
+  return ((row >> 7) * KT + kt) * kW4BlockRows + (row & 127);       // 32-bit words
+}
 
 __device__ __forceinline__ f16 h_from_bits(uint16_t b) { return __builtin_bit_cast(f16, b); }
 __device__ __forceinline__ uint16_t bits_from_h(f16 h) { return __builtin_bit_cast(uint16_t, h); }

@@ -173,7 +173,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
   const int KT = K / kBK;
   const int kt0 = blockIdx.y * kt_per_split;
   const int kt1 = min(KT, kt0 + kt_per_split);
-  const int64_t ldc = K / 2, ldp = K / kBK;
 
   // The k-loop below is written out by hand for the 256 x 256 tile of 8 waves (2 x 4),
   // each wave owning 128 x 64 outputs as 4 x 2 MFMA tiles of 32 x 32.
@@ -196,8 +195,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
   // word q of its 16-B piece becomes LDS chunk 4 (t & 1) + q of that row.
   const int b_row = tid >> 1, b_half = tid & 1;
   const int b_gn = n0 + b_row < N ? n0 + b_row : n0;
-  const uint8_t* const b_src = Wc + (int64_t)b_gn * ldc + b_half * 16;
-  const uint32_t* const p_src = Wp + (int64_t)b_gn * ldp;
+  const uint8_t* const b_src = Wc + w4_code_off(b_gn, 0, KT) + b_half * 16;
+  const uint32_t* const p_src = Wp + w4_param_idx(b_gn, 0, KT);
   const int b_lds0 = lds_off(b_row, b_half * 4 + 0), b_lds1 = lds_off(b_row, b_half * 4 + 1);
   const int b_lds2 = lds_off(b_row, b_half * 4 + 2), b_lds3 = lds_off(b_row, b_half * 4 + 3);
   uint4 ra0, ra1, ra2, ra3;         // A chunks of the next k-tile
@@ -233,8 +232,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
 #define STORE_A(j, BUF) *(uint4*)(sA + (BUF) * kStageA + a_lds + AROWS * 64 * j) = ra##j
 #define LOAD_B(SET, KT)                                   \
   do {                                                    \
-    rb_##SET = *(const uint4*)(b_src + (int64_t)(KT) * 32); \
-    rp_##SET = p_src[KT];                                 \
+    rb_##SET = *(const uint4*)(b_src + (int64_t)(KT) * kW4TileBytes); \
+    rp_##SET = p_src[(int64_t)(KT) * kW4BlockRows];                   \
   } while (0)
 #define DQ_SCALE(SET)                                     \
   do {                                                    \
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
   const int KT = K / kBK;
   const int kt0 = blockIdx.y * kt_per_split;
   const int kt1 = min(KT, kt0 + kt_per_split);
-  const int64_t ldc = K / 2, ldp = K / kBK;
 
   // A: thread t copies chunk (t & 7) of tile rows (t >> 3) + 32 j, j < MT.  Rows past M
   // read row m0 and are never stored.
@@ -400,10 +398,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
   // W row n0 + (2 w + j) 32 + l % 32, and that row's (offset, scale) word.
   const int b_n0 = n0 + wave * 64 + (lane & 31), b_n1 = b_n0 + 32;
   const int b_g0 = b_n0 < N ? b_n0 : 0, b_g1 = b_n1 < N ? b_n1 : 0;
-  const uint8_t* const b_src0 = Wc + (int64_t)b_g0 * ldc + g * 16;
-  const uint8_t* const b_src1 = Wc + (int64_t)b_g1 * ldc + g * 16;
-  const uint32_t* const p_src0 = Wp + (int64_t)b_g0 * ldp;
-  const uint32_t* const p_src1 = Wp + (int64_t)b_g1 * ldp;
+  const uint8_t* const b_src0 = Wc + w4_code_off(b_g0, 0, KT) + g * 16;
+  const uint8_t* const b_src1 = Wc + w4_code_off(b_g1, 0, KT) + g * 16;
+  const uint32_t* const p_src0 = Wp + w4_param_idx(b_g0, 0, KT);
+  const uint32_t* const p_src1 = Wp + w4_param_idx(b_g1, 0, KT);
   // W codes of four k-tiles in flight: set = (k-tile - kt0) mod 4
   uint4 rb0_0, rb1_0, rb0_1, rb1_1, rb0_2, rb1_2, rb0_3, rb1_3;
   uint32_t rp0_0, rp1_0, rp0_1, rp1_1, rp0_2, rp1_2, rp0_3, rp1_3;
@@ -429,10 +427,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
   if constexpr ((j) < MT) *(uint4*)(smem + (BUF) * kStageA + a_lds + 32 * 64 * (j)) = ra##BUF##_##j
 #define LOAD_B(SET, KT)                                       \
   do {                                                        \
-    rb0_##SET = *(const uint4*)(b_src0 + (int64_t)(KT) * 32); \
-    rb1_##SET = *(const uint4*)(b_src1 + (int64_t)(KT) * 32); \
-    rp0_##SET = p_src0[KT];                                   \
-    rp1_##SET = p_src1[KT];                                   \
+    rb0_##SET = *(const uint4*)(b_src0 + (int64_t)(KT) * kW4TileBytes); \
+    rb1_##SET = *(const uint4*)(b_src1 + (int64_t)(KT) * kW4TileBytes); \
+    rp0_##SET = p_src0[(int64_t)(KT) * kW4BlockRows];                   \
+    rp1_##SET = p_src1[(int64_t)(KT) * kW4BlockRows];                   \
   } while (0)
 #define DQ_SCALE(SET)                                         \
   do {                                                        \
@@ -551,6 +549,284 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
                           ep, Y, blockIdx.y);
 }
 
+// ------------------------------------------------------------------ decode kernel
+//
+// 64 < M <= 144 (the batch of a decode step).  At these sizes the product is bound
+// by streaming W, not by the matrix cores, and what limits the stream is how many
+// bytes are in flight per CU: with codes staged through registers only about one
+// k-tile fits, and vector loads complete in order, so the activation loads pin the
+// codes' lookahead too.  Here every operand goes straight from memory to LDS
+// (buffer loads with the LDS flag, no registers) through NST = 5 stages: the loads of
+// k-tile kt+4 are issued while kt is computed, three k-tiles of latency are hidden and
+// ~40 KB of W per CU is in flight.
+//
+// Stage layout: A [BM][64] fp16 with 16-byte chunk c of row r at position
+// c ^ ((r >> 1) & 7) (the swizzle is applied to the source addresses, since a direct
+// load writes lane i at base + 16 i); codes [384][32 B]; params [384] (offset, scale).
+// 16-row MFMA tiles (v_mfma_f32_16x16x32_f16), so M = 144 needs no padding: 8 waves
+// share the activation tile, each owns 48 columns (3 tiles of 16), a work-group
+// covers 384 columns.  In k-step s (32 wide) lane l (group g = l / 16) holds
+// k = 32 s + 8 g + e, e = 0..7: the code word at byte 16 s + 4 g of its row, and A chunk
+// 4 s + g (a k-step's 64 lanes read 16 rows x 4 consecutive chunks, which with the row
+// swizzle spreads over all banks: ~215 B/clk per CU against ~120 for chunks 2 g + s).  The B fragments of k-step 1 are dequantized during k-step 0, those
+// of the next k-tile's k-step 0 during k-step 1 (from the next stage, which the wait
+// at the top of the k-tile covers).
+template <int MT16>
+struct DecShape {
+  static constexpr int BM = MT16 * 16;
+  static constexpr int BN = 384;
+  static constexpr int THREADS = 512;
+  static constexpr int NST = 5;
+  static constexpr int A_BYTES = BM * kBK * 2;
+  static constexpr int C_BYTES = BN * 32;
+  static constexpr int P_BYTES = BN * 4;
+  static constexpr int STAGE_BYTES = A_BYTES + C_BYTES + P_BYTES;
+  static constexpr int A_INSTR = A_BYTES / 1024;   // 16-byte loads: 1 KB per wave instruction
+  static constexpr int C_INSTR = C_BYTES / 1024;
+  static constexpr int P_INSTR = P_BYTES / 256;    // 4-byte loads: 256 B per wave instruction
+  // every wave issues 4 sixteen-byte loads (A, else codes) and 1 four-byte load (params)
+  // per stage, so all waves count the same and the waits are compile-time constants
+  static constexpr int SLOTS = 5;
+  static_assert(A_INSTR + C_INSTR <= 32 && P_INSTR <= 8, "loads must fit the 5 slots of 8 waves");
+  static_assert(NST * STAGE_BYTES <= 160 * 1024, "stages must fit in LDS");
+};
+
+// Store one 16 x 16 MFMA accumulator tile: lane l holds column `col` and rows
+// row0 + 4 (l / 16) + r, r = 0..3.
+template <int OUT>
+__device__ __forceinline__ void store_acc16(const f32x4& a, int row0, int col, int M, int N,
+                                            const Epilogue& ep, void* __restrict__ Y,
+                                            int split) {
+  const int rl = row0 + 4 * ((threadIdx.x & 63) >> 4);
+  if (col >= N) return;
+  if constexpr (OUT == kOutF16) {
+    const float b = ep.bias ? (float)ep.bias[col] : 0.0f;
+    float res[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ep.residual) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (rl + r < M) res[r] = (float)ep.residual[(int64_t)(rl + r) * N + col];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (rl + r >= M) continue;
+      float v = a[r] + b;
+      if (ep.relu) v = fmaxf(v, 0.0f);
+      v += res[r];
+      ((f16*)Y)[(int64_t)(rl + r) * N + col] = (f16)v;
+    }
+  } else {
+    float* const y = (float*)Y + (OUT == kOutPartial ? (int64_t)split * M * N : 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (rl + r < M) y[(int64_t)(rl + r) * N + col] = a[r];
+  }
+}
+
+// s_waitcnt that waits for at most n outstanding vector-memory operations (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+#define DEC_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+// Work-group barrier without a fence (a fence would wait for every load in flight).
+// The bare barrier has no memory semantics for the compiler, so empty asm statements
+// with a memory clobber keep LDS accesses from moving across it.
+#define DEC_BARRIER()                  \
+  do {                                 \
+    asm volatile("" ::: "memory");     \
+    __builtin_amdgcn_s_barrier();      \
+    asm volatile("" ::: "memory");     \
+  } while (0)
+
+template <int MT16, int OUT>
+__global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
+    const f16* __restrict__ X, const uint8_t* __restrict__ Wc, const uint32_t* __restrict__ Wp,
+    int M, int N, int K, int kt_per_split, int ntiles, Epilogue ep, void* __restrict__ Y) {
+  using S = DecShape<MT16>;
+  constexpr int NST = S::NST;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[S::STAGE_BYTES], st1[S::STAGE_BYTES],
+      st2[S::STAGE_BYTES], st3[S::STAGE_BYTES], st4[S::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+
+  // work item: split-major, and each XCD (work-groups are dealt to the 8 XCDs in turn)
+  // takes a contiguous range, so the work-groups sharing an L2 mostly share a k-range
+  // of the activations
+  const int total = ntiles * (int)gridDim.y;
+  const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+  const int w = (total & 7) ? bid : (bid & 7) * (total >> 3) + (bid >> 3);
+  const int split = w / ntiles;
+  const int n0 = (w - split * ntiles) * S::BN;
+  const int KT = K / kBK;
+  const int kt0 = split * kt_per_split;
+  const int kt1 = min(KT, kt0 + kt_per_split);
+
+  // Buffer resources: X rows [0, M) and this block's three 128-row weight blocks (those
+  // that exist: rows are allocated in whole blocks).  Row and block offsets in the
+  // per-lane offset, the k-tile advance in the scalar offset: anything past the end is
+  // out of range and reads zeros.  (The host keeps the byte counts below 2^31.)
+  const int nblk = min((N - n0 + kW4BlockRows - 1) / kW4BlockRows, S::BN / kW4BlockRows);
+  const rsrc_t x_rs = make_rsrc(X, M * K * 2);
+  const rsrc_t w_rs = make_rsrc(Wc + w4_code_off(n0, 0, KT), nblk * KT * kW4TileBytes);
+  const rsrc_t p_rs = make_rsrc(Wp + w4_param_idx(n0, 0, KT), nblk * KT * kW4BlockRows * 4);
+
+  // Sixteen-byte slot i of this wave is instruction q = 4 wave + i of the stage: A rows
+  // 8 q .. 8 q + 7, else codes rows 32 q' .. 32 q' + 31 (1 KB of one weight block's
+  // contiguous 4 KB k-tile); the 4-byte slot of wave w < 6 loads params rows 64 w ..
+  // 64 w + 63 (256 contiguous bytes).  A slot with nothing left repeats instruction
+  // 0 of its kind (the same bytes to the same place), so every wave issues the same
+  // loads and every target stays inside its stage.  All choices are wave-uniform.
+#define DMA_SETUP(i)                                                                          \
+  int q##i = 4 * wave + (i);                                                                  \
+  if (q##i >= S::A_INSTR + S::C_INSTR) q##i = 0;                                              \
+  const bool isa##i = q##i < S::A_INSTR;                                                      \
+  const int qc##i = q##i - S::A_INSTR;                                                        \
+  const int ar##i = 8 * q##i + (lane >> 3);                                                   \
+  const rsrc_t rs##i = isa##i ? x_rs : w_rs;                                                  \
+  const int km##i = isa##i ? 128 : kW4TileBytes;                                              \
+  const int lo##i = isa##i ? q##i * 1024 : S::A_BYTES + qc##i * 1024;                         \
+  const int vo##i = isa##i ? (ar##i * K + (((lane & 7) ^ ((ar##i >> 1) & 7)) << 3)) * 2       \
+                           : (qc##i >> 2) * KT * kW4TileBytes + (qc##i & 3) * 1024 + lane * 16;
+  DMA_SETUP(0) DMA_SETUP(1) DMA_SETUP(2) DMA_SETUP(3)
+#undef DMA_SETUP
+  const int qp = wave < S::P_INSTR ? wave : 0;
+  const int lo4 = S::A_BYTES + S::C_BYTES + qp * 256;
+  const int vo4 = ((qp >> 1) * KT * kW4BlockRows + (qp & 1) * 64 + lane) * 4;
+#define LDSP(p) ((__attribute__((address_space(3))) void*)(p))
+#define ISSUE(ST, KT)                                                                         \
+  do {                                                                                        \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs0, LDSP(ST + lo0), 16, vo0, (KT) * km0, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs1, LDSP(ST + lo1), 16, vo1, (KT) * km1, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs2, LDSP(ST + lo2), 16, vo2, (KT) * km2, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs3, LDSP(ST + lo3), 16, vo3, (KT) * km3, 0, 0); \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(p_rs, LDSP(ST + lo4), 4, vo4, (KT) * 512, 0, 0); \
+  } while (0)
+
+  f16x8 fbc[3], fbn[3];   // B fragments: this / next k-step
+  uint32_t cw0, cw1, cw2, pw0, pw1, pw2, t0, t1;
+  f16x2 s2, m2;
+  f32x4 acc[MT16][3];
+#pragma unroll
+  for (int i = 0; i < MT16; ++i)
+#pragma unroll
+    for (int t = 0; t < 3; ++t) acc[i][t] = (f32x4){0, 0, 0, 0};
+
+  const int fa_base = ((lane & 15) * 64) * 2;                 // bytes
+  const int f_sw = ((lane & 15) >> 1) & 7;
+  const int c_off = S::A_BYTES + (48 * wave + (lane & 15)) * 32 + 4 * g;
+  const int p_off = S::A_BYTES + S::C_BYTES + (48 * wave + (lane & 15)) * 4;
+
+#define SB() __builtin_amdgcn_sched_barrier(0)
+#define FRAG_A(ST, KS, i) \
+  (*(const f16x8*)((ST) + fa_base + (i) * 16 * 128 + ((((4 * (KS) + g) ^ f_sw)) << 4)))
+// code word WORD (0: k-step 0, 1: k-step 1) and params of the 3 column tiles
+#define READ_W(ST, WORD)                                          \
+  do {                                                            \
+    cw0 = *(const uint32_t*)((ST) + c_off + 16 * (WORD));         \
+    cw1 = *(const uint32_t*)((ST) + c_off + 512 + 16 * (WORD));   \
+    cw2 = *(const uint32_t*)((ST) + c_off + 1024 + 16 * (WORD));  \
+    pw0 = *(const uint32_t*)((ST) + p_off);                       \
+    pw1 = *(const uint32_t*)((ST) + p_off + 64);                  \
+    pw2 = *(const uint32_t*)((ST) + p_off + 128);                 \
+  } while (0)
+#define DEQ(F, t, CW, PW)                                                           \
+  do {                                                                              \
+    s2 = h2_from_u32(((PW) >> 16) * 0x10001u);                                      \
+    m2 = h2_from_u32(((PW) & 0xFFFFu) * 0x10001u);                                  \
+    codes_to_bytes(CW, t0, t1);                                                     \
+    const f16x2 _d0 = dequant_pair(code_pair_f16<false>(t0), s2, m2);               \
+    const f16x2 _d1 = dequant_pair(code_pair_f16<true>(t0), s2, m2);                \
+    const f16x2 _d2 = dequant_pair(code_pair_f16<false>(t1), s2, m2);               \
+    const f16x2 _d3 = dequant_pair(code_pair_f16<true>(t1), s2, m2);                \
+    F[t] = (f16x8){_d0[0], _d0[1], _d1[0], _d1[1], _d2[0], _d2[1], _d3[0], _d3[1]}; \
+  } while (0)
+// one k-step: MT16 x 3 MFMAs with B fragments FB, A fragments read one row tile ahead;
+// after the MFMAs of row tile i: i = 0 reads code words WORD of stage WST, i = 1..3
+// dequantize them into FN
+#define KSTEP(ST, KS, FB, FN, WST, WORD)                                                      \
+  do {                                                                                        \
+    f16x8 _a0 = FRAG_A(ST, KS, 0), _a1 = _a0;                                                 \
+    _Pragma("unroll") for (int _i = 0; _i < MT16; ++_i) {                                    \
+      if (_i + 1 < MT16) {                                                                    \
+        if (_i & 1) _a0 = FRAG_A(ST, KS, _i + 1);                                             \
+        else _a1 = FRAG_A(ST, KS, _i + 1);                                                    \
+      }                                                                                       \
+      const f16x8 _a = (_i & 1) ? _a1 : _a0;                                                  \
+      acc[_i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[0], acc[_i][0], 0, 0, 0);   \
+      acc[_i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[1], acc[_i][1], 0, 0, 0);   \
+      acc[_i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[2], acc[_i][2], 0, 0, 0);   \
+      SB();                                                                                   \
+      if (_i == 0) READ_W(WST, WORD);                                                         \
+      if (_i == 1) DEQ(FN, 0, cw0, pw0);                                                      \
+      if (_i == 2) DEQ(FN, 1, cw1, pw1);                                                      \
+      if (_i == 3) DEQ(FN, 2, cw2, pw2);                                                      \
+      SB();                                                                                   \
+    }                                                                                         \
+  } while (0)
+// k-tile kt on stage ST (NXT: the stage of kt + 1, FREE: the stage of kt - 1, which
+// receives kt + 4): wait until this wave's loads of kt + 1 have landed (all but the two
+// later stages' 5 each), barrier, issue kt + 4, compute.  Past the last k-tile the
+// issue repeats the last one (L2 hits; that stage is never read), so every k-tile
+// issues exactly 5 loads and the counts stay exact.
+#define TILE(ST, NXT, FREE)                                                                   \
+  do {                                                                                        \
+    DEC_WAIT_VM(S::SLOTS * (NST - 3));                                                        \
+    DEC_BARRIER();                                                                            \
+    ISSUE(FREE, min(kt + NST - 1, klast));                                                    \
+    KSTEP(ST, 0, fbc, fbn, ST, 1);                                                            \
+    KSTEP(ST, 1, fbn, fbc, NXT, 0);                                                           \
+    ++kt;                                                                                     \
+  } while (0)
+
+  if (kt0 < kt1) {
+    const int klast = kt1 - 1;
+    int kt = kt0;
+    ISSUE(st0, kt0);
+    ISSUE(st1, min(kt0 + 1, klast));
+    ISSUE(st2, min(kt0 + 2, klast));
+    ISSUE(st3, min(kt0 + 3, klast));
+    DEC_WAIT_VM(S::SLOTS * (NST - 2));
+    DEC_BARRIER();
+    READ_W(st0, 0);
+    DEQ(fbc, 0, cw0, pw0);
+    DEQ(fbc, 1, cw1, pw1);
+    DEQ(fbc, 2, cw2, pw2);
+    // whole groups of NST k-tiles, then the 0..NST-1 left over (starting on stage 0);
+    // (a break after every k-tile makes the compiler spill the accumulators)
+    for (; kt + NST - 1 <= klast;) {
+      TILE(st0, st1, st4);
+      TILE(st1, st2, st0);
+      TILE(st2, st3, st1);
+      TILE(st3, st4, st2);
+      TILE(st4, st0, st3);
+    }
+    if (kt <= klast) TILE(st0, st1, st4);
+    if (kt <= klast) TILE(st1, st2, st0);
+    if (kt <= klast) TILE(st2, st3, st1);
+    if (kt <= klast) TILE(st3, st4, st2);
+    DEC_WAIT_VM(0);   // no load may land in LDS after the work-group ends
+  }
+#undef LDSP
+#undef ISSUE
+#undef SB
+#undef FRAG_A
+#undef READ_W
+#undef DEQ
+#undef KSTEP
+#undef TILE
+
+#pragma unroll
+  for (int i = 0; i < MT16; ++i)
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      store_acc16<OUT>(acc[i][t], i * 16, n0 + 48 * wave + 16 * t + (lane & 15), M, N, ep, Y,
+                       split);
+}
+#undef DEC_WAIT_VM
+#undef DEC_BARRIER
+
 // Sum of split-K partials in split order, then the epilogue.  4 elements per thread.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
@@ -589,7 +865,8 @@ struct Plan {
 };
 
 constexpr int kCfgBig = 0;      // M > 160: 256 x 256 tile, 8 waves (pipelined, dequant into LDS)
-constexpr int kCfgSkinny = 1;   // M <= 160: 32*ceil(M/32) x 256 tile, W streamed to registers
+constexpr int kCfgSkinny = 1;   // M <= 64 or 144 < M <= 160: 32*ceil(M/32) x 256 tile
+constexpr int kCfgDec = 2;      // 64 < M <= 144: 16*ceil(M/16) x 384 tile, 8 waves
 
 // Work-groups of the small-M kernel that one device runs at once (occupancy x CUs),
 // cached per device and tile height.
@@ -605,7 +882,19 @@ static int skinny_blocks_per_cu() {
   return n;
 }
 
-static int64_t skinny_concurrency(int mt) {
+template <int MT16>
+static int dec_blocks_per_cu() {
+  static int n = 0;
+  if (n == 0) {
+    int b = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &b, gemm_w4_dec_kernel<MT16, kOutPartial>, 512, 0);
+    n = b > 0 ? b : 1;
+  }
+  return n;
+}
+
+static int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   (void)hipGetDevice(&dev);
@@ -615,6 +904,22 @@ static int64_t skinny_concurrency(int mt) {
     (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     cus[slot] = n > 0 ? n : 256;
   }
+  return cus[slot];
+}
+
+static int64_t dec_concurrency(int mt16) {
+  int per_cu = 1;
+  switch (mt16) {
+    case 5: per_cu = dec_blocks_per_cu<5>(); break;
+    case 6: per_cu = dec_blocks_per_cu<6>(); break;
+    case 7: per_cu = dec_blocks_per_cu<7>(); break;
+    case 8: per_cu = dec_blocks_per_cu<8>(); break;
+    default: per_cu = dec_blocks_per_cu<9>(); break;
+  }
+  return (int64_t)per_cu * device_cus();
+}
+
+static int64_t skinny_concurrency(int mt) {
   int per_cu = 1;
   switch (mt) {
     case 1: per_cu = skinny_blocks_per_cu<1>(); break;
@@ -623,23 +928,25 @@ static int64_t skinny_concurrency(int mt) {
     case 4: per_cu = skinny_blocks_per_cu<4>(); break;
     default: per_cu = skinny_blocks_per_cu<5>(); break;
   }
-  return (int64_t)per_cu * cus[slot];
+  return (int64_t)per_cu * device_cus();
 }
 
 static Plan make_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes) {
   Plan p;
-  if (M <= 160) { p.cfg = kCfgSkinny; p.bm = (int)((M + 31) / 32) * 32; p.bn = 256; }
+  // (the decode kernel addresses X and its 384 W rows with 32-bit buffer offsets)
+  if (M > 64 && M <= 144 && K <= (1 << 22)) { p.cfg = kCfgDec; p.bm = (int)((M + 15) / 16) * 16; p.bn = 384; }
+  else if (M <= 160) { p.cfg = kCfgSkinny; p.bm = (int)((M + 31) / 32) * 32; p.bn = 256; }
   else { p.cfg = kCfgBig; p.bm = 256; p.bn = 256; }
   const int64_t KT = K / kBK;
   const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
   int splits = 1;
-  if (p.cfg == kCfgSkinny) {
-    // Split-K count of the small-M kernel from a cost model fitted on MI355X at the
+  if (p.cfg == kCfgSkinny || p.cfg == kCfgDec) {
+    // Split-K count of the small-M kernels from a cost model fitted on MI355X at the
     // decode shapes: time ~ rounds of resident work-groups x (a fixed cost of ~16
     // k-tiles per work-group + its k-tiles) + the partial sums written and reduced
     // (~4.75 MB per k-tile time).  Rounds matter: 576 work-groups on 256 CUs cost as
     // much as 768.
-    const int64_t conc = skinny_concurrency(p.bm / 32);
+    const int64_t conc = p.cfg == kCfgDec ? dec_concurrency(p.bm / 16) : skinny_concurrency(p.bm / 32);
     double best = 1e300;
     for (int64_t s = 1; s <= 8 && s <= KT; ++s) {
       const int64_t kps = (KT + s - 1) / s;
@@ -685,6 +992,17 @@ static void launch_big(const Plan& p, const f16* x, const flexq_w4* W, int M, Ep
                      (const uint32_t*)W->params, M, N, K, p.kt_per_split, ep, Y);
 }
 
+template <int MT16, int OUT>
+static void launch_dec(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
+                       void* Y, hipStream_t stream) {
+  using S = DecShape<MT16>;
+  const int N = (int)W->rows, K = (int)W->cols;
+  const int ntiles = (N + S::BN - 1) / S::BN;
+  dim3 grid(ntiles, p.splits);
+  hipLaunchKernelGGL((gemm_w4_dec_kernel<MT16, OUT>), grid, dim3(S::THREADS), 0, stream, x,
+                     W->codes, (const uint32_t*)W->params, M, N, K, p.kt_per_split, ntiles, ep, Y);
+}
+
 template <int MT, int OUT>
 static void launch_skinny(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
                           void* Y, hipStream_t stream) {
@@ -700,7 +1018,15 @@ static void launch_skinny(const Plan& p, const f16* x, const flexq_w4* W, int M,
 template <int OUT>
 static void launch_plan(const Plan& p, const f16* x, const flexq_w4* W, int M, Epilogue ep,
                         void* Y, hipStream_t stream) {
-  if (p.cfg == kCfgSkinny) {
+  if (p.cfg == kCfgDec) {
+    switch (p.bm / 16) {
+      case 5: launch_dec<5, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 6: launch_dec<6, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 7: launch_dec<7, OUT>(p, x, W, M, ep, Y, stream); break;
+      case 8: launch_dec<8, OUT>(p, x, W, M, ep, Y, stream); break;
+      default: launch_dec<9, OUT>(p, x, W, M, ep, Y, stream); break;
+    }
+  } else if (p.cfg == kCfgSkinny) {
     switch (p.bm / 32) {
       case 1: launch_skinny<1, OUT>(p, x, W, M, ep, Y, stream); break;
       case 2: launch_skinny<2, OUT>(p, x, W, M, ep, Y, stream); break;

@@ -81,9 +81,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
   int p = pos_base + (int)(m % seq) + 2;
   p = p >= pos_rows ? pos_rows - 1 : p;
+  const int KT = h / 64;
   for (int c = threadIdx.x; c < h / 16; c += blockDim.x) {
-    const uint2 cw = codes[(int64_t)tok * (h / 16) + c];
-    const uint32_t prm = params[(int64_t)tok * (h / 64) + c / 4];
+    // 16-element chunk c = bytes 8 (c % 4) .. +8 of k-tile c / 4 (4-bit weight layout)
+    const uint2 cw = codes[w4_code_off(tok, c / 4, KT) / 8 + (c & 3)];
+    const uint32_t prm = params[w4_param_idx(tok, c / 4, KT)];
     const f16x2 m2 = h2_from_u32((prm & 0xFFFFu) * 0x10001u);
     const f16x2 s2 = h2_from_u32((prm >> 16) * 0x10001u);
     f16x2 pr[8];

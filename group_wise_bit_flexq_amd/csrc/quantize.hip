@@ -14,15 +14,20 @@ constexpr int kQLanes = 4;                     // lanes per group
 constexpr int kQThreads = 256;
 constexpr int kQGroupsPerBlock = kQThreads / kQLanes;
 
+// WEIGHT = false: codes and params in row-major group order.  WEIGHT = true: the 4-bit
+// weight layout (blocks of 128 rows, k-tile major, see w4_code_off); ngroups then counts
+// the rows padded to a multiple of 128, and the groups of pad rows are stored as zeros.
+template <bool WEIGHT>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x,
                                                              uint2* __restrict__ codes,
                                                              uint32_t* __restrict__ params,
-                                                             int64_t ngroups) {
+                                                             int64_t ngroups, int64_t nreal,
+                                                             int64_t KT) {
   const int64_t g = (int64_t)blockIdx.x * kQGroupsPerBlock + threadIdx.x / kQLanes;
   const int part = threadIdx.x % kQLanes;
   // all lanes of a wave take part in the cross-lane reduction; lanes past the end
   // work on a copy of the last group and store nothing
-  const int64_t gl = g < ngroups ? g : ngroups - 1;
+  const int64_t gl = g < nreal ? g : nreal - 1;
   const uint4 a = x[gl * 8 + part * 2];
   const uint4 b = x[gl * 8 + part * 2 + 1];
   float v[16];
@@ -34,10 +39,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     v[2 * i + 1] = (float)h.y;
   }
   uint32_t packed[2];
-  const uint32_t p = GroupQ<kQLanes>::run(v, packed);
+  uint32_t p = GroupQ<kQLanes>::run(v, packed);
   if (g < ngroups) {
-    codes[g * 4 + part] = make_uint2(packed[0], packed[1]);
-    if (part == 0) params[g] = p;
+    if constexpr (WEIGHT) {
+      if (g >= nreal) packed[0] = packed[1] = p = 0;
+      const int64_t row = g / KT, kt = g - row * KT;
+      codes[w4_code_off(row, kt, KT) / 8 + part] = make_uint2(packed[0], packed[1]);
+      if (part == 0) params[w4_param_idx(row, kt, KT)] = p;
+    } else {
+      codes[g * 4 + part] = make_uint2(packed[0], packed[1]);
+      if (part == 0) params[g] = p;
+    }
   }
 }
 
@@ -75,20 +87,36 @@ extern "C" const char* flexq_status_string(int s) {
   }
 }
 
-extern "C" int flexq_quantize(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
-                              uint8_t* codes, uint16_t* params, hipStream_t stream) {
+static int quantize_entry(bool weight, const uint16_t* x, int64_t rows, int64_t cols,
+                          flexq_qconfig cfg, uint8_t* codes, uint16_t* params, hipStream_t stream) {
   if (cfg.num_bits != 4 || cfg.group_size != 64 || cfg.symmetric != 0) return FLEXQ_ERR_UNSUPPORTED;
   if (rows < 0 || cols <= 0 || cols % 64 != 0) return FLEXQ_ERR_INVALID;
   if (rows == 0) return FLEXQ_OK;
   if (!x || !codes || !params) return FLEXQ_ERR_INVALID;
   if (((uintptr_t)x & 15) || ((uintptr_t)codes & 7) || ((uintptr_t)params & 3)) return FLEXQ_ERR_INVALID;
-  const int64_t ngroups = rows * (cols / 64);
+  const int64_t KT = cols / 64;
+  const int64_t nreal = rows * KT;
+  const int64_t ngroups = weight ? (rows + kW4BlockRows - 1) / kW4BlockRows * kW4BlockRows * KT : nreal;
   const int64_t blocks = (ngroups + kQGroupsPerBlock - 1) / kQGroupsPerBlock;
   if (blocks > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(kQThreads), 0, stream,
-                     (const uint4*)x, (uint2*)codes, (uint32_t*)params, ngroups);
+  if (weight)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)blocks), dim3(kQThreads), 0, stream,
+                       (const uint4*)x, (uint2*)codes, (uint32_t*)params, ngroups, nreal, KT);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)blocks), dim3(kQThreads), 0, stream,
+                       (const uint4*)x, (uint2*)codes, (uint32_t*)params, ngroups, nreal, KT);
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
+}
+
+extern "C" int flexq_quantize(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
+                              uint8_t* codes, uint16_t* params, hipStream_t stream) {
+  return quantize_entry(false, x, rows, cols, cfg, codes, params, stream);
+}
+
+extern "C" int flexq_quantize_w4(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
+                                 uint8_t* codes, uint16_t* params, hipStream_t stream) {
+  return quantize_entry(true, x, rows, cols, cfg, codes, params, stream);
 }
 
 extern "C" int flexq_dequantize(const uint8_t* codes, const uint16_t* params, int64_t rows,

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libflexq.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3
 
 EXPORTED = (
-    "flexq_status_string", "flexq_quantize", "flexq_dequantize", "flexq_layernorm",
+    "flexq_status_string", "flexq_quantize", "flexq_quantize_w4", "flexq_dequantize",
+    "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
     "flexq_embed", "flexq_argmax", "flexq_layer_workspace_size", "flexq_prefill_layer",
@@ -85,6 +86,7 @@ def lib():
         sig = {
             "flexq_status_string": (C.c_char_p, [C.c_int]),
             "flexq_quantize": (C.c_int, [vp, i64, i64, QConfig, vp, vp, vp]),
+            "flexq_quantize_w4": (C.c_int, [vp, i64, i64, QConfig, vp, vp, vp]),
             "flexq_dequantize": (C.c_int, [vp, vp, i64, i64, vp, vp]),
             "flexq_layernorm": (C.c_int, [vp, i64, i64, i64, vp, vp, vp, vp]),
             "flexq_linear_w4_workspace_size": (sz, [i64, i64, i64]),
@@ -135,20 +137,62 @@ def _need(t, dtype, name):
 
 # ------------------------------------------------------------------ compressed tensors
 
-class W4:
-    """A 4-bit weight [rows][cols]: codes uint8 [rows][cols/2], params fp16 [rows][cols/64][2]."""
+class Q4:
+    """A group-wise 4-bit tensor [rows][cols] in row-major group order (flexq_quantize):
+    codes uint8 [rows][cols/2], params fp16 [rows][cols/64][2]."""
 
     def __init__(self, codes: torch.Tensor, params: torch.Tensor):
         self.codes, self.params = codes, params
         self.rows, self.cols = codes.shape[0], codes.shape[1] * 2
+
+    @staticmethod
+    def empty(rows, cols, device="cuda"):
+        return Q4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=device),
+                  torch.empty(rows, cols // 64, 2, dtype=torch.float16, device=device))
+
+
+W4_BLOCK_ROWS = 128
+
+
+class W4:
+    """A 4-bit weight [rows][cols] in the weight layout of flexq_w4: rows in blocks of
+    128, k-tile major.  codes uint8 [rows_pad/128][cols/64][128][32], params fp16
+    [rows_pad/128][cols/64][128][2] (rows_pad = rows rounded up to 128, pad rows zero)."""
+
+    def __init__(self, codes: torch.Tensor, params: torch.Tensor, rows: int):
+        if codes.dim() != 4 or codes.shape[2:] != (W4_BLOCK_ROWS, 32):
+            raise ValueError("W4 codes: expected [blocks][cols/64][128][32]")
+        self.codes, self.params = codes, params
+        self.rows, self.cols = rows, codes.shape[1] * 64
+        if codes.shape[0] * W4_BLOCK_ROWS < rows:
+            raise ValueError("W4 codes: fewer blocks than rows need")
 
     def c(self) -> W4Struct:
         return W4Struct(self.codes.data_ptr(), self.params.data_ptr(), self.rows, self.cols)
 
     @staticmethod
     def empty(rows, cols, device="cuda"):
-        return W4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=device),
-                  torch.empty(rows, cols // 64, 2, dtype=torch.float16, device=device))
+        nb, kt = (rows + W4_BLOCK_ROWS - 1) // W4_BLOCK_ROWS, cols // 64
+        return W4(torch.empty(nb, kt, W4_BLOCK_ROWS, 32, dtype=torch.uint8, device=device),
+                  torch.empty(nb, kt, W4_BLOCK_ROWS, 2, dtype=torch.float16, device=device), rows)
+
+    @staticmethod
+    def from_rowmajor(codes: torch.Tensor, params: torch.Tensor) -> "W4":
+        """Reorders row-major codes [rows][cols/2] and params [rows][cols/64][2] (as
+        flexq_quantize writes them) into the weight layout; a permutation, no arithmetic."""
+        rows, kt = codes.shape[0], codes.shape[1] // 32
+        nb = (rows + W4_BLOCK_ROWS - 1) // W4_BLOCK_ROWS
+        pad = nb * W4_BLOCK_ROWS - rows
+        c = torch.nn.functional.pad(codes, (0, 0, 0, pad)).view(nb, W4_BLOCK_ROWS, kt, 32)
+        p = torch.nn.functional.pad(params, (0, 0, 0, 0, 0, pad)).view(nb, W4_BLOCK_ROWS, kt, 2)
+        return W4(c.permute(0, 2, 1, 3).contiguous(), p.permute(0, 2, 1, 3).contiguous(), rows)
+
+    def rowmajor(self):
+        """(codes [rows][cols/2], params [rows][cols/64][2]) in row-major group order."""
+        nb, kt = self.codes.shape[0], self.codes.shape[1]
+        c = self.codes.permute(0, 2, 1, 3).reshape(nb * W4_BLOCK_ROWS, kt * 32)[:self.rows]
+        p = self.params.permute(0, 2, 1, 3).reshape(nb * W4_BLOCK_ROWS, kt, 2)[:self.rows]
+        return c, p
 
     def nbytes(self):
         return self.codes.numel() + self.params.numel() * 2
@@ -180,21 +224,34 @@ class KV4:
 QCFG = QConfig(4, 64, 0)
 
 
-def quantize(x: torch.Tensor, out: W4 | None = None, stream=None) -> W4:
+def quantize(x: torch.Tensor, out: Q4 | None = None, stream=None) -> Q4:
+    """Group-wise 4-bit quantization along the last dimension (row-major groups)."""
+    _need(x, torch.float16, "x")
+    rows = x.numel() // x.shape[-1]
+    cols = x.shape[-1]
+    q = out if out is not None else Q4.empty(rows, cols, x.device)
+    _check("flexq_quantize", lib().flexq_quantize(x.data_ptr(), rows, cols, QCFG,
+                                                  q.codes.data_ptr(), q.params.data_ptr(),
+                                                  _stream(stream)))
+    return q
+
+
+def quantize_weight(x: torch.Tensor, out: W4 | None = None, stream=None) -> W4:
+    """The same quantization written in the weight layout the GEMMs read (flexq_quantize_w4)."""
     _need(x, torch.float16, "x")
     rows = x.numel() // x.shape[-1]
     cols = x.shape[-1]
     w = out if out is not None else W4.empty(rows, cols, x.device)
-    _check("flexq_quantize", lib().flexq_quantize(x.data_ptr(), rows, cols, QCFG,
-                                                  w.codes.data_ptr(), w.params.data_ptr(),
-                                                  _stream(stream)))
+    _check("flexq_quantize_w4", lib().flexq_quantize_w4(x.data_ptr(), rows, cols, QCFG,
+                                                        w.codes.data_ptr(), w.params.data_ptr(),
+                                                        _stream(stream)))
     return w
 
 
-def dequantize(w: W4, stream=None) -> torch.Tensor:
-    out = torch.empty(w.rows, w.cols, dtype=torch.float16, device=w.codes.device)
-    _check("flexq_dequantize", lib().flexq_dequantize(w.codes.data_ptr(), w.params.data_ptr(),
-                                                      w.rows, w.cols, out.data_ptr(),
+def dequantize(q: Q4, stream=None) -> torch.Tensor:
+    out = torch.empty(q.rows, q.cols, dtype=torch.float16, device=q.codes.device)
+    _check("flexq_dequantize", lib().flexq_dequantize(q.codes.data_ptr(), q.params.data_ptr(),
+                                                      q.rows, q.cols, out.data_ptr(),
                                                       _stream(stream)))
     return out
 
@@ -313,9 +370,10 @@ class QLayer:
 
     @staticmethod
     def from_fp16(w16: dict, heads: int, device="cuda", stream=None):
-        """Quantizes the four matrices with flexq_quantize; vectors stay fp16."""
+        """Quantizes the four matrices with flexq_quantize_w4; vectors stay fp16."""
         vecs = {k: w16[k].to(device).contiguous() for k in QLayer.VECS}
-        mats = {k: quantize(w16[k].to(device).contiguous(), stream=stream) for k in QLayer.MATS}
+        mats = {k: quantize_weight(w16[k].to(device).contiguous(), stream=stream)
+                for k in QLayer.MATS}
         return QLayer(vecs, mats, heads)
 
     def c(self) -> LayerStruct:

@@ -104,7 +104,7 @@ def quant(reps):
     from group_wise_bit_flexq_amd.workloads import QUANT_4GIB
     rows, cols = QUANT_4GIB["rows"], QUANT_4GIB["cols"]
     x = synth.normal_fp16((rows, cols), 1.0, 5, device="cuda")
-    w = F.W4.empty(rows, cols)
+    w = F.Q4.empty(rows, cols)
     ms = _time(lambda: F.quantize(x, out=w), reps)
     nbytes = rows * cols * 2.5625
     return {"elements": rows * cols, "ms": ms, "gbps": nbytes / ms / 1e6}

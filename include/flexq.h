@@ -55,8 +55,24 @@ typedef struct {
   int32_t symmetric;
 } flexq_qconfig;
 
-/* A 4-bit weight matrix W[rows][cols] (rows = N outputs, cols = K inputs),
- * grouped along cols: codes [rows][cols/2], params [rows][cols/64][2]. */
+/* A 4-bit weight matrix W[rows][cols] (rows = N outputs, cols = K inputs), grouped
+ * along cols (one group = 64 columns = one k-tile), in the weight layout written by
+ * flexq_quantize_w4: rows in blocks of FLEXQ_W4_BLOCK_ROWS = 128, and within block b
+ * the k-tiles in order, each holding the block's 128 rows contiguously:
+ *   codes  byte  ((r / 128) * (cols/64) + kt) * 4096 + (r % 128) * 32 + j
+ *          holds elements 64 kt + 2 j (low nibble) and 64 kt + 2 j + 1 (high nibble)
+ *          of row r (j = 0..31);
+ *   params word  ((r / 128) * (cols/64) + kt) * 128 + (r % 128) = (offset, scale)
+ *          as two fp16 (offset in the low half) of group kt of row r.
+ * Both arrays cover rows padded up to a multiple of 128 (FLEXQ_W4_CODES_BYTES /
+ * FLEXQ_W4_PARAMS_BYTES); pad rows hold zeros.  Codes and params are those of
+ * flexq_quantize, only their order differs: a k-tile of any run of rows is read in
+ * whole cache lines, which streaming the weights at small batch needs. */
+#define FLEXQ_W4_BLOCK_ROWS 128
+#define FLEXQ_W4_CODES_BYTES(rows, cols) \
+  ((((rows) + 127) / 128) * 128 * (int64_t)(cols) / 2)
+#define FLEXQ_W4_PARAMS_BYTES(rows, cols) \
+  ((((rows) + 127) / 128) * 128 * (int64_t)(cols) / 16)
 typedef struct {
   const uint8_t* codes;
   const uint16_t* params;
@@ -142,7 +158,14 @@ const char* flexq_status_string(int status);
 int flexq_quantize(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
                    uint8_t* codes, uint16_t* params, hipStream_t stream);
 
-/* Inverse of flexq_quantize for weights (`decompress`): out fp16 [rows][cols] =
+/* The same quantization as flexq_quantize, written in the 4-bit weight layout of
+ * flexq_w4 (codes FLEXQ_W4_CODES_BYTES(rows, cols) bytes, params
+ * FLEXQ_W4_PARAMS_BYTES(rows, cols) bytes, pad rows written as zeros).  codes 8-byte
+ * and params 4-byte aligned; same errors as flexq_quantize. */
+int flexq_quantize_w4(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
+                      uint8_t* codes, uint16_t* params, hipStream_t stream);
+
+/* Inverse of flexq_quantize (row-major codes and params, `decompress`): out fp16 [rows][cols] =
  * fp16(code * scale + offset) with one rounding.  A test and inspection aid; the
  * GEMMs dequantize inside their own tiles. */
 int flexq_dequantize(const uint8_t* codes, const uint16_t* params, int64_t rows, int64_t cols,

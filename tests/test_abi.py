@@ -1,0 +1,66 @@
+"""The C-ABI boundary on the CPU: the built library loads and exports every function
+include/flexq.h declares (nothing is called: there is no GPU here), the binding's
+symbol list is the header's, and the host-side reordering into the 4-bit weight
+layout matches the byte/word formulas the header documents."""
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "flexq.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(flexq_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("flexq_quantize", "flexq_quantize_w4", "flexq_linear_w4", "flexq_attn_prefill",
+              "flexq_attn_decode_kv4", "flexq_decode_step"):
+        assert n in names, n
+
+
+def test_binding_lists_exactly_the_header_functions():
+    from group_wise_bit_flexq_amd import flexq as F
+    assert sorted(F.EXPORTED) == _declared()
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    from group_wise_bit_flexq_amd import flexq as F
+    if not os.path.exists(F.LIB_PATH):
+        pytest.skip("libflexq.so not built (run __graft_entry__.build())")
+    lib = F.lib()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (130, 192), (256, 128), (300, 640)])
+def test_weight_layout_reordering_matches_header_formulas(rows, cols):
+    from group_wise_bit_flexq_amd import flexq as F
+    rng = np.random.default_rng(rows + cols)
+    codes = rng.integers(0, 256, size=(rows, cols // 2)).astype(np.uint8)
+    params = rng.integers(0, 65536, size=(rows, cols // 64, 2)).astype(np.uint16)
+    w = F.W4.from_rowmajor(torch.from_numpy(codes), torch.from_numpy(params.view(np.float16)))
+    KT, nb = cols // 64, (rows + 127) // 128
+    flat_c = w.codes.numpy().reshape(-1)
+    flat_p = w.params.numpy().view(np.uint32).reshape(-1)
+    assert flat_c.size == nb * 128 * cols // 2 and flat_p.size == nb * 128 * KT
+    for r in range(rows):
+        for kt in range(KT):
+            b = ((r // 128) * KT + kt) * 4096 + (r % 128) * 32
+            assert np.array_equal(flat_c[b:b + 32], codes[r, 32 * kt:32 * kt + 32])
+            assert flat_p[((r // 128) * KT + kt) * 128 + r % 128] == params[r, kt].view(np.uint32)[0]
+    pad_rows = [r for r in range(rows, nb * 128)]
+    for r in pad_rows[:5]:
+        b = ((r // 128) * KT) * 4096 + (r % 128) * 32
+        assert not flat_c[b:b + 32].any()
+    c2, p2 = w.rowmajor()
+    assert np.array_equal(c2.numpy(), codes)
+    assert np.array_equal(p2.numpy().view(np.uint16), params)

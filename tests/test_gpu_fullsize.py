@@ -32,7 +32,7 @@ def _check_linear(x_gpu, w16_gpu, wq, y_gpu, rng, what, bias=None, res=None, rel
     ns = rng.integers(0, N, n)
     wrows = to_np(w16_gpu[torch.from_numpy(ns).cuda()])
     codes, params = O.quantize(wrows)
-    assert np.array_equal(codes, to_np(wq.codes[torch.from_numpy(ns).cuda()])), what + " codes"
+    assert np.array_equal(codes, to_np(wq.rowmajor()[0][torch.from_numpy(ns).cuda()])), what + " codes"
     xs = to_np(x_gpu[torch.from_numpy(ms).cuda()])
     b = None if bias is None else to_np(bias)[ns]
     r = None if res is None else to_np(res[torch.from_numpy(ms).cuda(), torch.from_numpy(ns).cuda()])

@@ -51,11 +51,45 @@ def test_quantize_bit_exact(rows, cols):
     assert np.array_equal(to_np(w.params).view(np.uint16), params.view(np.uint16))
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 64), (200, 768), (384, 128), (3, 12288)])
+def test_quantize_weight_layout_bit_exact(rows, cols):
+    """flexq_quantize_w4: the oracle's codes and params, placed where flexq_w4 says
+    (checked through the documented byte/word formulas), pad rows zero."""
+    F = require_gpu()
+    _say("quantize_w4", rows, cols)
+    rng = np.random.default_rng(rows * 17 + cols)
+    x = _groups_mix(rng, rows, cols)
+    w = F.quantize_weight(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    codes, params = O.quantize(x)
+    flat_c = to_np(w.codes).reshape(-1)
+    flat_p = to_np(w.params).view(np.uint32).reshape(-1)
+    KT = cols // 64
+    r = np.arange(rows)[:, None]
+    kt = np.arange(KT)[None, :]
+    base = ((r // 128) * KT + kt) * 4096 + (r % 128) * 32
+    got_c = flat_c[base[:, :, None] + np.arange(32)[None, None, :]].reshape(rows, cols // 2)
+    assert np.array_equal(got_c, codes)
+    got_p = flat_p[((r // 128) * KT + kt) * 128 + (r % 128)]
+    assert np.array_equal(got_p, params.view(np.uint32).reshape(rows, KT))
+    nb = (rows + 127) // 128
+    assert flat_c.size == nb * 128 * cols // 2
+    pad = np.ones((nb * 128, KT), bool)
+    pad[:rows] = False
+    prow = np.nonzero(pad[:, 0])[0]
+    if prow.size:
+        pb = ((prow[:, None] // 128) * KT + kt) * 4096 + (prow[:, None] % 128) * 32
+        assert not flat_c[pb[:, :, None] + np.arange(32)].any()
+        assert not flat_p[((prow[:, None] // 128) * KT + kt) * 128 + prow[:, None] % 128].any()
+    c2, p2 = w.rowmajor()
+    assert np.array_equal(to_np(c2), codes)
+
+
 def test_quantize_rejects_bad_config():
     F = require_gpu()
     import ctypes as C
     x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
-    w = F.W4.empty(4, 64)
+    w = F.Q4.empty(4, 64)
     L = F.lib()
     st = L.flexq_quantize(x.data_ptr(), 4, 64, F.QConfig(3, 64, 0), w.codes.data_ptr(),
                           w.params.data_ptr(), C.c_void_p(0))
@@ -75,7 +109,7 @@ def test_dequantize_bit_exact():
     s = (np.abs(rng.normal(size=(rows, cols // 64))) * 2.0 ** rng.integers(-26, 10, size=(rows, cols // 64))).astype(F16)
     m = (rng.normal(size=(rows, cols // 64)) * 2.0 ** rng.integers(-20, 12, size=(rows, cols // 64))).astype(F16)
     params = np.stack([m, s], axis=-1).astype(F16)
-    w = F.W4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
+    w = F.Q4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
     got = to_np(F.dequantize(w))
     ref = O.dequantize_weight(codes, params)
     assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
@@ -87,7 +121,8 @@ def _bound_linear(x, w16, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 200, 320), (32, 384, 1024), (37, 128, 256),
-                                   (64, 256, 512), (144, 384, 768), (160, 128, 128),
+                                   (64, 256, 512), (80, 1152, 384), (129, 1000, 1024), (144, 384, 768),
+                                   (160, 128, 128),
                                    (300, 256, 640), (513, 192, 1024), (4, 256, 8192)])
 @pytest.mark.parametrize("epi", ["plain", "bias_relu", "bias_res"])
 def test_linear_w4(M, N, K, epi):
@@ -100,7 +135,7 @@ def test_linear_w4(M, N, K, epi):
     res = rng.normal(size=(M, N)).astype(F16) if epi == "bias_res" else None
     relu = epi == "bias_relu"
     codes, params = O.quantize(w)
-    wq = F.W4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
+    wq = F.W4.from_rowmajor(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
     y = F.linear_w4(torch.from_numpy(x).cuda(), wq,
                     bias=None if bias is None else torch.from_numpy(bias).cuda(),
                     residual=None if res is None else torch.from_numpy(res).cuda(), relu=relu)
@@ -118,7 +153,7 @@ def test_linear_w4_f32(M, N, K):
     x = rng.normal(size=(M, K)).astype(F16)
     w = (rng.normal(size=(N, K)) * 0.05).astype(F16)
     codes, params = O.quantize(w)
-    wq = F.W4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
+    wq = F.W4.from_rowmajor(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
     got = to_np(F.linear_w4_f32(torch.from_numpy(x).cuda(), wq)).astype(np.float64)
     ref = O.linear_w4(x, codes, params, out_dtype=np.float64)
     wd = O.dequantize_weight(codes, params)
@@ -134,7 +169,7 @@ def test_linear_in_place_residual():
     w = (rng.normal(size=(N, K)) * 0.05).astype(F16)
     r = rng.normal(size=(M, N)).astype(F16)
     codes, params = O.quantize(w)
-    wq = F.W4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
+    wq = F.W4.from_rowmajor(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
     rt = torch.from_numpy(r).cuda()
     F.linear_w4(torch.from_numpy(x).cuda(), wq, residual=rt, out=rt)
     ref = O.linear_w4(x, codes, params, residual=r)
@@ -220,7 +255,7 @@ def test_embed_and_argmax():
     e16 = (rng.normal(size=(V, h)) * 0.5).astype(F16)
     pos = rng.normal(size=(40, h)).astype(F16)
     codes, params = O.quantize(e16)
-    ew = F.W4(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
+    ew = F.W4.from_rowmajor(torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda())
     toks = rng.integers(0, V, size=12).astype(np.int32)
     got = to_np(F.embed(torch.from_numpy(toks).cuda(), 3, 4, ew, torch.from_numpy(pos).cuda()))
     ref = O.embed(toks, 3 + np.arange(12) % 4, codes, params, pos)

@@ -40,8 +40,9 @@ def test_layer_opt125m_ops_teacher_forced():
     oq = {}
     for k in F.QLayer.MATS:
         oq[k] = O.quantize(wn[k])
-        assert np.array_equal(to_np(L.m[k].codes), oq[k][0]), k
-        assert np.array_equal(to_np(L.m[k].params).view(np.uint16), oq[k][1].view(np.uint16)), k
+        c, p = L.m[k].rowmajor()
+        assert np.array_equal(to_np(c), oq[k][0]), k
+        assert np.array_equal(to_np(p).view(np.uint16), oq[k][1].view(np.uint16)), k
     wd = {k: O.dequantize_weight(*oq[k]) for k in oq}
     kv = F.KV4(B, nh, hd, S + G)
     oc = O.KVCache(B, nh, hd, S + G)
@@ -120,7 +121,7 @@ def _host_model(h, nh, f, V, L, seed):
 def _gpu_model(F, parts, nh, batch, max_len, rows):
     layers16, emb, pos, g, b = parts
     layers = [F.QLayer.from_fp16(w, nh) for w in layers16]
-    return F.QModel(layers, F.quantize(emb.cuda()), pos.cuda(), g.cuda(), b.cuda(), nh, batch,
+    return F.QModel(layers, F.quantize_weight(emb.cuda()), pos.cuda(), g.cuda(), b.cuda(), nh, batch,
                     max_len, rows)
 
 
