@@ -16,10 +16,8 @@
         cache of 2048 + 64 positions);
     python -m group_wise_bit_flexq_amd.kernel_probe copy --mib 1024 --reps 3
         an elementwise device copy of a known size, the reference that scales the
-        HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above;
-    python -m group_wise_bit_flexq_amd.kernel_probe read --mib 2048 --reps 5
-        a device-wide sum over a tensor of that size: a measured read-stream rate of
-        HBM, beside the nominal 8 TB/s, for the decode kernels (which mostly read).
+        HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above, and a
+        measured HBM rate (read + write) beside the nominal 8 TB/s.
 Each prints its per-launch times (HIP events) as one JSON line.
 """
 from __future__ import annotations
@@ -139,18 +137,9 @@ def copy(mib, reps):
     return {"bytes_read": 2 * n, "bytes_written": 2 * n, "ms": ms, "gbps": 4 * n / ms / 1e6}
 
 
-def read(mib, reps):
-    import torch
-    n = mib * (1 << 20) // 2
-    src = torch.randn(n, device="cuda").half()
-    ms = _time(lambda: torch.sum(src, dtype=torch.float32), reps)
-    return {"bytes_read": 2 * n, "ms": ms, "gbps": 2 * n / ms / 1e6}
-
-
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "stress", "copy",
-                                     "read"])
+    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "stress", "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -169,8 +158,6 @@ def main():
         r = quant(a.reps)
     elif a.what == "stress":
         r = stress(a.reps)
-    elif a.what == "read":
-        r = read(a.mib, a.reps)
     else:
         r = copy(a.mib, a.reps)
     print(json.dumps({"probe": a.what, "workload": a.workload, "results": r}), flush=True)

@@ -122,6 +122,7 @@ def _bound_linear(x, w16, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 200, 320), (32, 384, 1024), (37, 128, 256),
                                    (64, 256, 512), (80, 1152, 384), (129, 1000, 1024), (144, 384, 768),
+                                   (100, 200, 64), (144, 64, 4096),
                                    (160, 128, 128),
                                    (300, 256, 640), (513, 192, 1024), (4, 256, 8192)])
 @pytest.mark.parametrize("epi", ["plain", "bias_relu", "bias_res"])
