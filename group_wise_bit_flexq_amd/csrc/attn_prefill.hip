@@ -21,7 +21,7 @@
 //    each 16-lane group, lane j points at 4 dims of key j / 4 and lane i receives
 //    dim i of the 4 keys.
 // After the loop the work-group quantizes K and V of its own 128 positions into the
-// cache (8 lanes per 64-element group), reading them from the staged LDS tiles.
+// cache (4 lanes per 64-element group), reading them from the staged LDS tiles.
 #include "quant_dev.h"
 
 namespace flexq {
@@ -241,28 +241,38 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   // block 2 qb + i sits in stage i; the last block's stores preceded the last barrier)
   constexpr int GPT = HD / 64;                     // groups per token vector
   constexpr int NGROUPS = QB * GPT * 2;            // K and V
-  const int sub = tid & 7;
-  for (int gi = tid >> 3; gi < NGROUPS; gi += 32) {
+  // 4 lanes per 64-element group (16 elements each, two 16-B chunks): a wave
+  // quantizes 16 groups per pass
+  const int sub = tid & 3;
+  for (int gi = tid >> 2; gi < NGROUPS; gi += 64) {
     const int isv = gi / (QB * GPT);
     const int rem = gi % (QB * GPT);
     const int tr = rem / GPT;                      // position within the 128
     const int grp = rem % GPT;
     const int tok = q0 + tr;
     const int stg = tr / KB, row = tr % KB;
-    const int ch = grp * 8 + sub;
-    f16x8 xv;
-    if (isv) xv = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8);
-    else xv = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch));
-    float x[8];
+    const int ch = grp * 8 + sub * 2;
+    f16x8 xa, xb;
+    if (isv) {
+      xa = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8);
+      xb = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8 + 8);
+    } else {
+      xa = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch));
+      xb = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch + 1));
+    }
+    float x[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)xv[e];
-    uint32_t packed[1];
-    const uint32_t prm = GroupQ<8>::run(x, packed);
+    for (int e = 0; e < 8; ++e) {
+      x[e] = (float)xa[e];
+      x[8 + e] = (float)xb[e];
+    }
+    uint32_t packed[2];
+    const uint32_t prm = GroupQ<4>::run(x, packed);
     if (tok < S) {
       const int64_t slot = ((int64_t)(b0 + b) * kv.nh + head) * kv.max_len + tok;
       uint8_t* cbase = isv ? kv.vc : kv.kc;
       uint32_t* pbase = isv ? kv.vp : kv.kp;
-      *(uint32_t*)(cbase + slot * (HD / 2) + grp * 32 + sub * 4) = packed[0];
+      *(uint2*)(cbase + slot * (HD / 2) + grp * 32 + sub * 8) = make_uint2(packed[0], packed[1]);
       if (sub == 0) pbase[slot * GPT + grp] = prm;
     }
   }
