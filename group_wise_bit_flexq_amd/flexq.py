@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_PKG, "libflexq.so")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3
 
 EXPORTED = (
-    "flexq_status_string", "flexq_quantize", "flexq_quantize_w4", "flexq_dequantize",
-    "flexq_layernorm",
+    "flexq_status_string", "flexq_quantize", "flexq_quantize_w4", "flexq_quantize_ex",
+    "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
     "flexq_embed", "flexq_argmax", "flexq_layer_workspace_size", "flexq_prefill_layer",
@@ -87,6 +87,8 @@ def lib():
             "flexq_status_string": (C.c_char_p, [C.c_int]),
             "flexq_quantize": (C.c_int, [vp, i64, i64, QConfig, vp, vp, vp]),
             "flexq_quantize_w4": (C.c_int, [vp, i64, i64, QConfig, vp, vp, vp]),
+            "flexq_quantize_ex": (C.c_int, [vp, i64, i64, i64, QConfig, vp, vp, vp]),
+            "flexq_dequantize_ex": (C.c_int, [vp, vp, i64, i64, i64, QConfig, vp, vp]),
             "flexq_dequantize": (C.c_int, [vp, vp, i64, i64, vp, vp]),
             "flexq_layernorm": (C.c_int, [vp, i64, i64, i64, vp, vp, vp, vp]),
             "flexq_linear_w4_workspace_size": (sz, [i64, i64, i64]),
@@ -253,6 +255,50 @@ def dequantize(q: Q4, stream=None) -> torch.Tensor:
     _check("flexq_dequantize", lib().flexq_dequantize(q.codes.data_ptr(), q.params.data_ptr(),
                                                       q.rows, q.cols, out.data_ptr(),
                                                       _stream(stream)))
+    return out
+
+
+def _split_dims(shape, group_dim):
+    gd = group_dim % len(shape)
+    outer = 1
+    for d in shape[:gd]:
+        outer *= d
+    inner = 1
+    for d in shape[gd + 1:]:
+        inner *= d
+    return gd, outer, shape[gd], inner
+
+
+def quantize_ex(x: torch.Tensor, num_bits=4, group_size=64, group_dim=-1, symmetric=False,
+                stream=None):
+    """General compression config (flexq_quantize_ex): returns (codes, params) with codes
+    uint8 shape[:gd] + (ng * group_size * num_bits / 8,) + shape[gd+1:] and params fp16
+    shape[:gd] + (ng,) + shape[gd+1:] + (2,), ng = ceil(shape[gd] / group_size)."""
+    _need(x, torch.float16, "x")
+    shape = tuple(x.shape)
+    gd, outer, n, inner = _split_dims(shape, group_dim)
+    ng = -(-n // group_size)
+    gb = group_size * num_bits // 8
+    codes = torch.empty(shape[:gd] + (ng * gb,) + shape[gd + 1:], dtype=torch.uint8, device=x.device)
+    params = torch.empty(shape[:gd] + (ng,) + shape[gd + 1:] + (2,), dtype=torch.float16,
+                         device=x.device)
+    cfg = QConfig(num_bits, group_size, 1 if symmetric else 0)
+    _check("flexq_quantize_ex", lib().flexq_quantize_ex(x.data_ptr(), outer, n, inner, cfg,
+                                                        codes.data_ptr(), params.data_ptr(),
+                                                        _stream(stream)))
+    return codes, params
+
+
+def dequantize_ex(codes: torch.Tensor, params: torch.Tensor, n, num_bits=4, group_size=64,
+                  group_dim=-1, symmetric=False, stream=None) -> torch.Tensor:
+    """fp16 values of `quantize_ex`'s output, the grouped axis back to its n elements."""
+    shape = tuple(codes.shape)
+    gd, outer, _, inner = _split_dims(shape, group_dim)
+    out = torch.empty(shape[:gd] + (n,) + shape[gd + 1:], dtype=torch.float16, device=codes.device)
+    cfg = QConfig(num_bits, group_size, 1 if symmetric else 0)
+    _check("flexq_dequantize_ex", lib().flexq_dequantize_ex(codes.data_ptr(), params.data_ptr(),
+                                                            outer, n, inner, cfg, out.data_ptr(),
+                                                            _stream(stream)))
     return out
 
 

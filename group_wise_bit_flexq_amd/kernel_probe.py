@@ -11,6 +11,9 @@
         heads) with the fused 4-bit KV store;
     python -m group_wise_bit_flexq_amd.kernel_probe quant --reps 3
         the standalone quantizer on a 4 GiB fp16 tensor [524288][4096];
+    python -m group_wise_bit_flexq_amd.kernel_probe quant_ex --reps 3
+        the general-config quantizer on the same tensor at 3 bits, group 64, asymmetric
+        (groups along the rows, and along the columns: group_dim 0);
     python -m group_wise_bit_flexq_amd.kernel_probe stress --reps 3
         decode attention of the KV-compression stress shape (batch 64, 56 heads x 128,
         cache of 2048 + 64 positions);
@@ -111,6 +114,22 @@ def quant(reps):
     return {"elements": rows * cols, "ms": ms, "gbps": nbytes / ms / 1e6}
 
 
+def quant_ex(reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    from group_wise_bit_flexq_amd.workloads import QUANT_4GIB
+    rows, cols = QUANT_4GIB["rows"], QUANT_4GIB["cols"]
+    x = synth.normal_fp16((rows, cols), 1.0, 5, device="cuda")
+    nbytes = rows * cols * (2 + 3 / 8 + 4 / 64)
+    res = {}
+    for name, gd in (("innermost", -1), ("group_dim0", 0)):
+        ms = _time(lambda: F.quantize_ex(x, 3, 64, gd), reps)
+        res[name] = {"elements": rows * cols, "ms": ms, "gbps": nbytes / ms / 1e6}
+    return res
+
+
 def stress(reps):
     import torch
 
@@ -139,7 +158,8 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "stress", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "quant_ex", "stress",
+                                     "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -156,6 +176,8 @@ def main():
         r = prefill_attn(wl, a.reps)
     elif a.what == "quant":
         r = quant(a.reps)
+    elif a.what == "quant_ex":
+        r = quant_ex(a.reps)
     elif a.what == "stress":
         r = stress(a.reps)
     else:

@@ -165,6 +165,34 @@ int flexq_quantize(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig 
 int flexq_quantize_w4(const uint16_t* x, int64_t rows, int64_t cols, flexq_qconfig cfg,
                       uint8_t* codes, uint16_t* params, hipStream_t stream);
 
+/* General compression config (walkthrough section 6.3 names num_bits, group_size,
+ * group_dim and symmetric; the hub page mentions int3/int4).  x fp16 seen as
+ * [outer][n][inner], grouped along n in groups of cfg.group_size consecutive positions
+ * (inner = 1 when the grouped axis is the innermost one; any other group_dim is the
+ * product split of the shape around it).  cfg: num_bits 2..8, group_size 1..4096 with
+ * group_size * num_bits a multiple of 8, symmetric 0 or 1; else FLEXQ_ERR_UNSUPPORTED.
+ * A ragged last group is zero-padded and the padding quantized with it.  Per group,
+ * fp32, contraction off:
+ *   asymmetric: step = fp16((max - min) / (2^b - 1)), code = clamp(rne((x - min) *
+ *               (1 / step)), 0, 2^b - 1), offset = min (+0 for a zero minimum);
+ *   symmetric:  B = 2^(b-1) - 1, step = fp16(max|x| / B), code = clamp(rne(x * (1 /
+ *               step)), -B, B) + 2^(b-1), offset = +0;
+ *   constant (asymmetric) / all-zero (symmetric) group: step 0; a step that
+ *   underflows fp16 becomes 2^-24.
+ * Outputs (ng = ceil(n / group_size), gb = group_size * num_bits / 8):
+ *   codes  uint8 [outer][ng * gb][inner]: the b-bit codes of a group concatenated
+ *          least significant bit first into gb bytes along n;
+ *   params (offset, step) fp16 pairs [outer][ng][inner].
+ * x 2-byte and params 4-byte aligned; bit-identical to the oracle. */
+int flexq_quantize_ex(const uint16_t* x, int64_t outer, int64_t n, int64_t inner,
+                      flexq_qconfig cfg, uint8_t* codes, uint16_t* params, hipStream_t stream);
+
+/* Inverse of flexq_quantize_ex: out fp16 [outer][n][inner] = fp16(code * step + offset),
+ * or fp16((code - 2^(b-1)) * step) if symmetric, one rounding of the exact value; the
+ * padding of a ragged last group is not written. */
+int flexq_dequantize_ex(const uint8_t* codes, const uint16_t* params, int64_t outer, int64_t n,
+                        int64_t inner, flexq_qconfig cfg, uint16_t* out, hipStream_t stream);
+
 /* Inverse of flexq_quantize (row-major codes and params, `decompress`): out fp16 [rows][cols] =
  * fp16(code * scale + offset) with one rounding.  A test and inspection aid; the
  * GEMMs dequantize inside their own tiles. */

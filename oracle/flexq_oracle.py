@@ -132,6 +132,112 @@ def dequantize_kv(codes, params) -> np.ndarray:
     return dequantize_exact(codes, params)
 
 
+# ----------------------------------------------------------------------------- general config
+
+def pack_bits(c: np.ndarray, num_bits: int) -> np.ndarray:
+    """[..., n] codes in [0, 2^b) -> [..., n*b/8] bytes: the codes are concatenated
+    least significant bit first (bit k of element i is bit b*i + k of the stream,
+    stream bit t is bit t % 8 of byte t // 8).  For b = 4 this is `pack_nibbles`."""
+    c = np.asarray(c, dtype=np.uint64)
+    n = c.shape[-1]
+    assert (n * num_bits) % 8 == 0
+    bits = ((c[..., :, None] >> np.arange(num_bits, dtype=np.uint64)) & 1).astype(np.uint8)
+    bits = bits.reshape(c.shape[:-1] + (n * num_bits // 8, 8))
+    return (bits << np.arange(8, dtype=np.uint8)).sum(axis=-1).astype(np.uint8)
+
+
+def unpack_bits(b: np.ndarray, num_bits: int) -> np.ndarray:
+    """Inverse of `pack_bits`: [..., m] bytes -> [..., m*8/b] codes."""
+    b = np.asarray(b, dtype=np.uint8)
+    bits = ((b[..., :, None] >> np.arange(8, dtype=np.uint8)) & 1).astype(np.uint64)
+    n = b.shape[-1] * 8 // num_bits
+    bits = bits.reshape(b.shape[:-1] + (n, num_bits))
+    return (bits << np.arange(num_bits, dtype=np.uint64)).sum(axis=-1).astype(np.uint16)
+
+
+def quantize_config(x, num_bits=4, group_size=64, group_dim=-1, symmetric=False):
+    """Group-wise quantization with a general CompressionConfig ([WALK] section 6.3
+    names its fields num_bits, group_size, group_dim, symmetric; section 1.2 of the
+    hub page mentions int3 and int4).  Readings where the pages are silent:
+      * the grouped axis is zero-padded to a whole number of groups; the padding is
+        quantized with its group like any element (`dequantize_config` drops it);
+      * asymmetric: offset = group minimum, step = fp16(fl32(max - min) / (2^b - 1)),
+        code = clamp(rne(fl32(x - min) * fl32(1 / step)), 0, 2^b - 1) -- the 4-bit
+        rule with 15 replaced by 2^b - 1;
+      * symmetric: B = 2^(b-1) - 1, step = fp16(fl32(max |x|) / B),
+        code = clamp(rne(fl32(x) * fl32(1 / step)), -B, B), stored as code + 2^(b-1)
+        (b unsigned bits), offset stored as +0;
+      * a constant (asymmetric) or all-zero (symmetric) group gets step 0 and the
+        code of its value; a step that underflows fp16 becomes 2^-24; a zero offset
+        is stored as +0;
+      * the b-bit codes of a group are packed with `pack_bits` into group_size*b/8
+        bytes (group_size*b must be a multiple of 8), so the packed tensor has
+        shape[:group_dim] + (num_groups * group_size * b / 8,) + shape[group_dim+1:]
+        (the pages' data_shape with b = 4), and params has
+        shape[:group_dim] + (num_groups,) + shape[group_dim+1:] + (2,) = (offset, step).
+    Decisions are taken in fp32 in a fixed order, as in `quantize`."""
+    if not 2 <= num_bits <= 8:
+        raise ValueError("num_bits must be in [2, 8]")
+    if group_size < 1 or (group_size * num_bits) % 8:
+        raise ValueError("group_size * num_bits must be a multiple of 8")
+    x = np.asarray(x, dtype=F16)
+    gd = group_dim % x.ndim
+    xm = np.moveaxis(x, gd, -1)
+    n = xm.shape[-1]
+    ng = -(-n // group_size)
+    pad = ng * group_size - n
+    xp = np.concatenate([xm, np.zeros(xm.shape[:-1] + (pad,), F16)], axis=-1) if pad else xm
+    g = xp.reshape(xm.shape[:-1] + (ng, group_size)).astype(F32)
+    if symmetric:
+        qmax = (1 << (num_bits - 1)) - 1
+        amax = np.abs(g).max(axis=-1)
+        s = (amax / F32(qmax)).astype(F16)
+        const = amax == 0
+    else:
+        qmax = (1 << num_bits) - 1
+        mn = g.min(axis=-1)
+        mx = g.max(axis=-1)
+        s = ((mx - mn) / F32(qmax)).astype(F16)
+        const = mx == mn
+    s = np.where(const, F16(0), np.where(s == 0, F16(2.0 ** -24), s)).astype(F16)
+    s32 = s.astype(F32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(const, F32(0), F32(1) / np.where(const, F32(1), s32)).astype(F32)
+    if symmetric:
+        t = g * inv[..., None]
+        c = np.clip(np.rint(t), -qmax, qmax).astype(np.int32) + (1 << (num_bits - 1))
+        offset = np.zeros(s.shape, F16)
+    else:
+        t = (g - mn[..., None]) * inv[..., None]
+        c = np.clip(np.rint(t), 0, qmax).astype(np.int32)
+        offset = (mn + F32(0)).astype(F16)
+    packed = pack_bits(c.reshape(c.shape[:-2] + (ng * group_size,)), num_bits)
+    codes = np.moveaxis(packed, -1, gd)
+    params = np.moveaxis(np.stack([offset, s], axis=-1).astype(F16), -2, gd)
+    return codes, params
+
+
+def dequantize_config(codes, params, n, num_bits=4, group_size=64, group_dim=-1,
+                      symmetric=False) -> np.ndarray:
+    """Exact values (float64) of `quantize_config`'s output, the grouped axis cut back
+    to its n elements: code * step + offset, or (code - 2^(b-1)) * step if symmetric."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    gd = group_dim % codes.ndim
+    cm = np.moveaxis(codes, gd, -1)
+    pm = np.moveaxis(np.asarray(params, dtype=F16), gd, -2)
+    c = unpack_bits(cm, num_bits).astype(F64)
+    ng = pm.shape[-2]
+    c = c.reshape(cm.shape[:-1] + (ng, group_size))
+    off = pm[..., 0].astype(F64)[..., None]
+    step = pm[..., 1].astype(F64)[..., None]
+    if symmetric:
+        v = (c - (1 << (num_bits - 1))) * step
+    else:
+        v = c * step + off
+    v = v.reshape(cm.shape[:-1] + (ng * group_size,))[..., :n]
+    return np.moveaxis(v, -1, gd)
+
+
 # ----------------------------------------------------------------------------- linear / LN
 
 def _finish_linear(acc, bias, residual, relu, out_dtype):
