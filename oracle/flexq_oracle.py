@@ -40,7 +40,12 @@ Readings of the pages where they leave a step open (each also listed in DESIGN.m
   * OPT layer: pre-LayerNorm (eps 1e-5), biases on all projections, ReLU FFN,
     1/sqrt(head_dim) applied to the score, learned positions with offset 2, final
     LayerNorm, LM head tied to the 4-bit token embedding without bias, greedy argmax
-    with the lowest index winning ties.
+    with the lowest index winning ties;
+  * sampling ([WALK] section 4.1 do_sample / temperature; [NOTES] "Flex Opt" Task and
+    stopped flags): a draw from softmax(logits / T) taken by the Gumbel-max rule in
+    float64, its uniforms from SplitMix64 (a counter-based generator, implemented on
+    each side from its published definition) keyed by (seed, step, sequence, token);
+    a sequence that produces the stop token is stopped and produces it from then on.
 """
 from __future__ import annotations
 
@@ -439,6 +444,63 @@ def lm_head(x_last, lnf_g, lnf_b, e_codes, e_params, e_w64=None):
     return logits, np.argmax(logits, axis=-1).astype(np.int32)
 
 
+# ----------------------------------------------------------------------------- sampling
+
+GOLDEN64 = 0x9E3779B97F4A7C15
+
+
+def splitmix64(seed: int, counter) -> np.ndarray:
+    """Output number `counter` (0, 1, ...) of the SplitMix64 generator started from
+    state `seed`: mix(seed + (counter + 1) * golden) with the published constants
+    (0x9E3779B97F4A7C15; multipliers 0xBF58476D1CE4E5B9, 0x94D049BB133111EB; shifts 30,
+    27, 31), arithmetic mod 2^64 -- a counter-based generator."""
+    c = np.asarray(counter, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + (c + np.uint64(1)) * np.uint64(GOLDEN64)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def sample_uniform(seed: int, step: int, rows, n: int) -> np.ndarray:
+    """Uniform draws in (0, 1), one per (sequence, token) of generation step `step`:
+    counter = step * 2^48 + sequence * 2^32 + token, u = ((z >> 11) + 1/2) * 2^-53."""
+    rows = np.asarray(rows, dtype=np.uint64)[:, None]
+    tok = np.arange(n, dtype=np.uint64)[None, :]
+    counter = (np.uint64(step) << np.uint64(48)) | (rows << np.uint64(32)) | tok
+    z = splitmix64(seed, counter)
+    return ((z >> np.uint64(11)).astype(F64) + 0.5) * 2.0 ** -53
+
+
+def pick(logits, gen=None, step=0, m0=0, stopped=None):
+    """Next tokens from fp32 logits [M][N] ([WALK] section 4.1: `generate(input_ids,
+    do_sample, temperature, max_new_tokens, stop)`).  Readings where the pages are
+    silent:
+      * do_sample=False: greedy, the lowest index among equal maxima;
+      * do_sample=True: a draw from softmax(logits / temperature) by the Gumbel-max
+        rule: argmax_n (logit_n / T + g_n), g_n = -log(-log u_n) with the counter-based
+        uniforms of `sample_uniform` (sequence m0 + m, step = the position of the
+        token the logits follow), in float64, lowest index among equal maxima;
+      * stop (a token id, or -1 for none): a sequence that has produced it is stopped
+        and keeps producing it; `stopped` (bool [M], updated in place) carries that
+        across steps.
+    `gen` is None or a dict with do_sample, temperature, seed, stop."""
+    lg = np.asarray(logits, dtype=np.float32)
+    M, N = lg.shape
+    if gen is not None and gen.get("do_sample"):
+        u = sample_uniform(gen["seed"], step, np.arange(m0, m0 + M), N)
+        score = lg.astype(F64) / F64(np.float32(gen["temperature"])) - np.log(-np.log(u))
+        nxt = score.argmax(axis=1)
+    else:
+        nxt = lg.argmax(axis=1)
+    nxt = nxt.astype(np.int64)
+    stop = -1 if gen is None else int(gen.get("stop", -1))
+    if stopped is not None and stop >= 0:
+        nxt = np.where(stopped, stop, nxt)
+        stopped |= nxt == stop
+    return nxt
+
+
 class QModel:
     """OPT-shaped model: embedding, N decoder layers, output head ([NOTES] "Flex Opt")."""
 
@@ -473,14 +535,20 @@ class QModel:
             x = L.decode(x, pos, c, b0)
         return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
-    def generate(self, tokens, gen):
-        """Greedy generation of `gen` tokens ([WALK] section 4.1, do_sample=False)."""
+    def generate(self, tokens, gen, config=None):
+        """Generation of `gen` tokens ([WALK] section 4.1): greedy without `config`, else
+        `pick` with it (do_sample, temperature, seed, stop)."""
         tokens = np.asarray(tokens)
         nb, seq = tokens.shape
         caches = self.new_caches(nb, seq + gen - 1)
-        _, nxt = self.prefill(tokens, caches)
+        stopped = np.zeros(nb, dtype=bool)
+        lg, nxt = self.prefill(tokens, caches)
+        if config is not None:
+            nxt = pick(lg, config, seq - 1, 0, stopped)
         out = [nxt]
         for i in range(gen - 1):
-            _, nxt = self.decode_step(nxt, seq + i, caches)
+            lg, nxt = self.decode_step(nxt, seq + i, caches)
+            if config is not None:
+                nxt = pick(lg, config, seq + i, 0, stopped)
             out.append(nxt)
         return np.stack(out, axis=1)
