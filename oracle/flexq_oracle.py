@@ -464,12 +464,14 @@ def splitmix64(seed: int, counter) -> np.ndarray:
 
 def sample_uniform(seed: int, step: int, rows, n: int) -> np.ndarray:
     """Uniform draws in (0, 1), one per (sequence, token) of generation step `step`:
-    counter = step * 2^48 + sequence * 2^32 + token, u = ((z >> 11) + 1/2) * 2^-53."""
+    counter = step * 2^48 + sequence * 2^32 + token, u = ((z >> 12) + 1/2) * 2^-52,
+    the top 52 bits of the output centred in their cell (exact in float64, so u lies in
+    [2^-53, 1 - 2^-53])."""
     rows = np.asarray(rows, dtype=np.uint64)[:, None]
     tok = np.arange(n, dtype=np.uint64)[None, :]
     counter = (np.uint64(step) << np.uint64(48)) | (rows << np.uint64(32)) | tok
     z = splitmix64(seed, counter)
-    return ((z >> np.uint64(11)).astype(F64) + 0.5) * 2.0 ** -53
+    return ((z >> np.uint64(12)).astype(F64) + 0.5) * 2.0 ** -52
 
 
 def pick(logits, gen=None, step=0, m0=0, stopped=None):

@@ -20,6 +20,10 @@ def test_splitmix64_published_sequences():
 def test_uniforms_are_open_interval_and_uniform():
     u = O.sample_uniform(7, 3, np.arange(64), 4096).reshape(-1)
     assert np.all(u > 0) and np.all(u < 1)
+    # u is the generator's top 52 bits, centred: output number 3 * 2^48 + 5 * 2^32 + 7
+    # for step 3, sequence 5, token 7
+    z = int(O.splitmix64(7, np.array([3 * 2**48 + 5 * 2**32 + 7], np.uint64))[0])
+    assert O.sample_uniform(7, 3, [5], 8)[0, 7] == ((z >> 12) + 0.5) / 2.0**52
     # Kolmogorov-Smirnov statistic of 262144 draws against U(0, 1)
     s = np.sort(u)
     n = s.size
@@ -54,7 +58,7 @@ def test_greedy_is_argmax_with_lowest_index_on_ties():
 
 def test_low_temperature_sampling_is_greedy(rng):
     # logits on a 1/64 grid with distinct maxima: at T = 1e-6 the gap over T dwarfs the
-    # Gumbel noise, which stays within [-3.7, 37.5] for 53-bit uniforms
+    # Gumbel noise, which stays within [-3.7, 36.8] for uniforms in [2^-53, 1 - 2^-53]
     lg = (rng.permutation(np.arange(300 * 50)) / 64.0).astype(np.float32).reshape(300, 50)
     gen = dict(do_sample=True, temperature=1e-6, seed=3, stop=-1)
     assert np.array_equal(O.pick(lg, gen, step=9), lg.argmax(axis=1))
