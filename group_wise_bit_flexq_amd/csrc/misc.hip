@@ -116,19 +116,32 @@ __device__ __forceinline__ void better(float& v, int& i, float v2, int i2) {
   }
 }
 
-// One work-group per row: largest logit, lowest index among equal maxima.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int64_t N,
-                                                     int32_t* __restrict__ next) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  const float* r = logits + (int64_t)blockIdx.x * N;
+__device__ __forceinline__ void better(double& v, int& i, double v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+// SplitMix64: output number c from state `seed` is mix(seed + (c + 1) * golden), with
+// the published golden-ratio increment, mixing multipliers and shifts (64-bit
+// wrap-around arithmetic).  `splitmix64_mix` takes the already-advanced state.
+constexpr uint64_t kGolden64 = 0x9E3779B97F4A7C15ull;
+__device__ __forceinline__ uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Block-wide reduction of (value, index) pairs; the result is valid in thread 0.
+template <int THREADS, typename T>
+__device__ __forceinline__ void block_best(T& bv, int& bi) {
+  __shared__ T sv[THREADS / 64];
+  __shared__ int si[THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int64_t n = tid; n < N; n += 256) better(bv, bi, r[n], (int)n);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(bv, o, 64);
+    const T v2 = __shfl_xor(bv, o, 64);
     const int i2 = __shfl_xor(bi, o, 64);
     better(bv, bi, v2, i2);
   }
@@ -137,9 +150,60 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ l
     si[wave] = bi;
   }
   __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
-    next[blockIdx.x] = bi == 0x7FFFFFFF ? 0 : bi;
+  if (tid == 0)
+    for (int w = 1; w < THREADS / 64; ++w) better(bv, bi, sv[w], si[w]);
+}
+
+// Next token of one row per work-group.  Greedy: the largest logit.  Sampling: the
+// Gumbel-max draw argmax_n (logit_n / T - log(-log u_n)) in fp64, u_n from
+// SplitMix64 output (step << 48 | sequence << 32 | n) mapped to ((z >> 12) + 1/2) 2^-52.
+// Lowest index among equal maxima in both.  With a stop token, a row already
+// stopped emits it again, and a row that emits it becomes stopped (`fresh`: the
+// incoming flags are ignored, as for the first token of a sequence).
+template <bool SAMPLE, int THREADS>
+__global__ __launch_bounds__(THREADS) void pick_kernel(const float* __restrict__ logits, int64_t N,
+                                                       uint64_t seed, double temperature,
+                                                       uint32_t step, uint32_t m0, int32_t stop,
+                                                       int32_t* __restrict__ stopped, int fresh,
+                                                       int32_t* __restrict__ next) {
+  const int m = blockIdx.x;
+  if (stopped && !fresh && stopped[m]) {  // uniform over the work-group
+    if (threadIdx.x == 0) next[m] = stop;
+    return;
+  }
+  const float* r = logits + (int64_t)m * N;
+  int bi = 0x7FFFFFFF;
+  if constexpr (SAMPLE) {
+    // counter c = step << 48 | sequence << 32 | n with n < 2^32, so the state
+    // seed + (c + 1) * golden advances by THREADS * golden from one n to the next
+    const uint64_t base = ((uint64_t)step << 48) | ((uint64_t)(m0 + m) << 32);
+    uint64_t state = seed + (base + threadIdx.x + 1) * kGolden64;
+    double bv = -INFINITY;
+    for (int64_t n = threadIdx.x; n < N; n += THREADS, state += (uint64_t)THREADS * kGolden64) {
+      const uint64_t z = splitmix64_mix(state);
+      const double u = ((double)(z >> 12) + 0.5) * 0x1p-52;
+      const double s = (double)r[n] / temperature - log(-log(u));
+      better(bv, bi, s, (int)n);
+    }
+    block_best<THREADS>(bv, bi);
+  } else {
+    // four loads in flight per lane before the compares (the loop is latency-bound)
+    float bv = -INFINITY;
+    int64_t n = threadIdx.x;
+    for (; n + 3 * THREADS < N; n += 4 * THREADS) {
+      const float v0 = r[n], v1 = r[n + THREADS], v2 = r[n + 2 * THREADS], v3 = r[n + 3 * THREADS];
+      better(bv, bi, v0, (int)n);
+      better(bv, bi, v1, (int)(n + THREADS));
+      better(bv, bi, v2, (int)(n + 2 * THREADS));
+      better(bv, bi, v3, (int)(n + 3 * THREADS));
+    }
+    for (; n < N; n += THREADS) better(bv, bi, r[n], (int)n);
+    block_best<THREADS>(bv, bi);
+  }
+  if (threadIdx.x == 0) {
+    const int t = bi == 0x7FFFFFFF ? 0 : bi;
+    next[m] = t;
+    if (stopped) stopped[m] = (stop >= 0 && t == stop) ? 1 : (fresh ? 0 : stopped[m]);
   }
 }
 
@@ -182,13 +246,42 @@ extern "C" int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, i
   return FLEXQ_OK;
 }
 
-extern "C" int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next,
-                            hipStream_t stream) {
+namespace flexq {
+
+int launch_pick(const float* logits, int64_t M, int64_t N, const flexq_gen_config* gen,
+                int32_t step, int32_t m0, int32_t* stopped, bool fresh, int32_t* next,
+                hipStream_t stream) {
   if (M < 0 || N <= 0 || N > 0x7FFFFFFF) return FLEXQ_ERR_INVALID;
   if (M == 0) return FLEXQ_OK;
   if (!logits || !next) return FLEXQ_ERR_INVALID;
   if (M > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)M), dim3(256), 0, stream, logits, N, next);
+  const bool sample = gen && gen->do_sample;
+  const int32_t stop = gen ? gen->stop : -1;
+  if (gen && stop >= N) return FLEXQ_ERR_INVALID;
+  if (stop < 0) stopped = nullptr;
+  if (sample) {
+    if (!(gen->temperature > 0.0f) || !(gen->temperature <= __FLT_MAX__)) return FLEXQ_ERR_INVALID;
+    if (step < 0 || step > 0xFFFF || m0 < 0 || (int64_t)m0 + M > 0x10000) return FLEXQ_ERR_INVALID;
+    hipLaunchKernelGGL((pick_kernel<true, 1024>), dim3((unsigned)M), dim3(1024), 0, stream, logits,
+                       N, gen->seed, (double)gen->temperature, (uint32_t)step, (uint32_t)m0, stop,
+                       stopped, (int)fresh, next);
+  } else {
+    hipLaunchKernelGGL((pick_kernel<false, 1024>), dim3((unsigned)M), dim3(1024), 0, stream, logits,
+                       N, (uint64_t)0, 1.0, 0u, 0u, stop, stopped, (int)fresh, next);
+  }
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
+}
+
+}  // namespace flexq
+
+extern "C" int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next,
+                            hipStream_t stream) {
+  return launch_pick(logits, M, N, nullptr, 0, 0, nullptr, false, next, stream);
+}
+
+extern "C" int flexq_pick(const float* logits, int64_t M, int64_t N, const flexq_gen_config* gen,
+                          int32_t step, int32_t m0, int32_t* stopped, int32_t* next,
+                          hipStream_t stream) {
+  return launch_pick(logits, M, N, gen, step, m0, stopped, false, next, stream);
 }

@@ -216,15 +216,19 @@ static int model_scratch(const flexq_model* m, int64_t rows, int32_t batch, int3
   return FLEXQ_OK;
 }
 
+// Final LayerNorm, tied LM head and the token choice for cache rows b0 .. b0+nb-1
+// whose logits follow position `step`; `fresh` at prefill (a sequence's first token).
 static int model_head(const flexq_model* m, const uint16_t* x_last, int64_t stride, int32_t nb,
-                      int32_t* next, float* logits, const ModelScratch& s, hipStream_t stream) {
+                      int32_t b0, int32_t step, bool fresh, int32_t* next, float* logits,
+                      const ModelScratch& s, hipStream_t stream) {
   TRY(flexq_layernorm(x_last, nb, m->hidden, stride, m->lnf_g, m->lnf_b, s.lnf, stream));
   float* lg = logits ? logits : s.logits;
   {
     TraceScope ts(m->trace, stream, FLEXQ_TRACE_HEAD, nb);
     TRY(flexq_linear_w4_f32(s.lnf, nb, &m->embed, lg, s.head_ws, s.head_ws_bytes, stream));
   }
-  TRY(flexq_argmax(lg, nb, m->vocab, next, stream));
+  TRY(flexq::launch_pick(lg, nb, m->vocab, m->gen, step, b0, m->stopped ? m->stopped + b0 : nullptr,
+                  fresh, next, stream));
   return FLEXQ_OK;
 }
 
@@ -247,8 +251,8 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
                   stream, m->trace));
     std::swap(x, y);
   }
-  return model_head(m, x + (int64_t)(S - 1) * m->hidden, (int64_t)S * m->hidden, nb, next, logits,
-                    s, stream);
+  return model_head(m, x + (int64_t)(S - 1) * m->hidden, (int64_t)S * m->hidden, nb, b0, S - 1,
+                    true, next, logits, s, stream);
 }
 
 extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, int32_t B,
@@ -269,5 +273,5 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
                   stream, m->trace));
     std::swap(x, y);
   }
-  return model_head(m, x, m->hidden, B, next, logits, s, stream);
+  return model_head(m, x, m->hidden, B, 0, pos, false, next, logits, s, stream);
 }

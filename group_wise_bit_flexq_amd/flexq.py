@@ -21,7 +21,7 @@ EXPORTED = (
     "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
-    "flexq_embed", "flexq_argmax", "flexq_layer_workspace_size", "flexq_prefill_layer",
+    "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
 )
 
@@ -61,13 +61,20 @@ class TraceStruct(C.Structure):
                 ("rows", C.POINTER(C.c_int64)), ("capacity", C.c_int32), ("count", C.c_int32)]
 
 
+class GenConfig(C.Structure):
+    """flexq_gen_config: greedy or temperature sampling, optional stop token."""
+    _fields_ = [("do_sample", C.c_int32), ("temperature", C.c_float), ("seed", C.c_uint64),
+                ("stop", C.c_int32)]
+
+
 class ModelStruct(C.Structure):
     _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("pos_rows", C.c_int32),
                 ("layer", C.POINTER(LayerStruct)), ("kv", C.POINTER(KV4Struct)),
                 ("embed", W4Struct), ("pos", C.c_void_p), ("lnf_g", C.c_void_p),
                 ("lnf_b", C.c_void_p), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct))]
+                ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct)),
+                ("gen", C.POINTER(GenConfig)), ("stopped", C.c_void_p)]
 
 
 _lib = None
@@ -100,6 +107,7 @@ def lib():
                                                 sz, vp]),
             "flexq_embed": (C.c_int, [vp, i64, i32, i32, C.POINTER(W4Struct), vp, i32, vp, vp]),
             "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
+            "flexq_pick": (C.c_int, [vp, i64, i64, C.POINTER(GenConfig), i32, i32, vp, vp, vp]),
             "flexq_layer_workspace_size": (sz, [i32, i32, i32, i64, i32]),
             "flexq_prefill_layer": (C.c_int, [C.POINTER(LayerStruct), C.POINTER(KV4Struct), i32,
                                               i32, i32, vp, i32, i32, i32, vp, vp, sz, vp]),
@@ -398,6 +406,24 @@ def argmax(logits, out=None, stream=None):
     return y
 
 
+def gen_config(do_sample=False, temperature=1.0, seed=0, stop=-1):
+    return GenConfig(int(bool(do_sample)), float(temperature), int(seed) & (2**64 - 1), int(stop))
+
+
+def pick(logits, gen=None, step=0, m0=0, stopped=None, out=None, stream=None):
+    """Next tokens from fp32 logits [M][N] (flexq_pick); `gen` a GenConfig or None,
+    `stopped` None or a device int32 [M] tensor updated in place."""
+    M, N = logits.shape
+    _need(logits, torch.float32, "logits")
+    y = out if out is not None else torch.empty(M, dtype=torch.int32, device=logits.device)
+    if stopped is not None:
+        _need(stopped, torch.int32, "stopped")
+    _check("flexq_pick", lib().flexq_pick(logits.data_ptr(), M, N,
+                                          None if gen is None else C.byref(gen), step, m0,
+                                          _ptr(stopped), y.data_ptr(), _stream(stream)))
+    return y
+
+
 # ------------------------------------------------------------------ layers and models
 
 class QLayer:
@@ -487,6 +513,16 @@ class QModel:
                                    pos16.shape[0], self._layer_arr, self._kv_arr, embed_w4.c(),
                                    pos16.data_ptr(), lnf_g.data_ptr(), lnf_b.data_ptr(),
                                    self.workspace.data_ptr(), nbytes)
+
+    def set_generation(self, gen=None):
+        """Greedy (None) or a GenConfig for the following prefill / decode calls; with a
+        stop token the model keeps device stopped flags, one per cache row."""
+        self._gen = gen
+        self._struct.gen = None if gen is None else C.pointer(gen)
+        self.stopped = None
+        if gen is not None and gen.stop >= 0:
+            self.stopped = torch.zeros(self.batch, dtype=torch.int32, device=self.workspace.device)
+        self._struct.stopped = _ptr(self.stopped)
 
     def prefill(self, tokens, b0=0, logits=None, next_out=None, stream=None):
         _need(tokens, torch.int32, "tokens")

@@ -17,6 +17,9 @@
     python -m group_wise_bit_flexq_amd.kernel_probe stress --reps 3
         decode attention of the KV-compression stress shape (batch 64, 56 heads x 128,
         cache of 2048 + 64 positions);
+    python -m group_wise_bit_flexq_amd.kernel_probe pick --workload opt175b --reps 5
+        the token choice of one decode step (batch x vocab fp32 logits): greedy, and
+        temperature sampling with a stop token;
     python -m group_wise_bit_flexq_amd.kernel_probe copy --mib 1024 --reps 3
         an elementwise device copy of a known size, the reference that scales the
         HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above, and a
@@ -147,6 +150,21 @@ def stress(reps):
     return {"T": T + 1, "ms": ms, "gbps": nbytes / ms / 1e6}
 
 
+def pick(wl, reps):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    M, N = wl.batch, wl.vocab
+    lg = torch.randn(M, N, device="cuda") * 3
+    out = torch.empty(M, dtype=torch.int32, device="cuda")
+    stopped = torch.zeros(M, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, gen in (("greedy", None), ("sample_t0.7_stop", F.gen_config(True, 0.7, 1, 2))):
+        ms = _time(lambda: F.pick(lg, gen, step=100, stopped=stopped, out=out), reps)
+        res[name] = {"M": M, "N": N, "ms": ms, "logit_gbps": M * N * 4 / ms / 1e6}
+    return res
+
+
 def copy(mib, reps):
     import torch
     n = mib * (1 << 20) // 2
@@ -159,7 +177,7 @@ def copy(mib, reps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "quant_ex", "stress",
-                                     "copy"])
+                                     "pick", "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -180,6 +198,8 @@ def main():
         r = quant_ex(a.reps)
     elif a.what == "stress":
         r = stress(a.reps)
+    elif a.what == "pick":
+        r = pick(wl, a.reps)
     else:
         r = copy(a.mib, a.reps)
     print(json.dumps({"probe": a.what, "workload": a.workload, "results": r}), flush=True)

@@ -128,6 +128,25 @@ typedef struct {
   int32_t count;
 } flexq_trace;
 
+/* Token choice of a generation (walkthrough section 4.1, `generate(..., do_sample,
+ * temperature, ..., stop)`; source notes "Flex Opt": the Task's temperature and
+ * stop token, the per-sequence stopped flags).
+ *   do_sample 0: greedy, the largest logit (lowest index among equal maxima).
+ *   do_sample 1: a draw from softmax(logits / temperature) by the Gumbel-max rule:
+ *     argmax_n (logit_n / T - log(-log u_n)) in fp64, lowest index on ties, with
+ *     u_n = ((z >> 12) + 1/2) 2^-52 and z the SplitMix64 output number
+ *     step * 2^48 + sequence * 2^32 + n from state `seed` (seed + (c + 1) *
+ *     0x9E3779B97F4A7C15, then the published mix).  The draw depends only on
+ *     (seed, step, sequence, n): not on the batch split or the launch.
+ *   stop: a token id in [0, vocab), or -1 for none.  A sequence that emits it is
+ *     stopped and emits it at every later step. */
+typedef struct {
+  int32_t do_sample;
+  float temperature; /* > 0 and finite when do_sample */
+  uint64_t seed;
+  int32_t stop;
+} flexq_gen_config;
+
 /* A whole OPT-shaped model.  Non-owning: every pointer stays the caller's.
  * `layer` and `kv` are HOST arrays of `layers` entries (the structs inside hold
  * device pointers).  embed is the 4-bit token embedding [vocab][hidden], also used
@@ -144,6 +163,14 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   flexq_trace* trace; /* NULL, or a HOST trace (see flexq_trace) */
+  /* NULL (greedy), or a HOST generation config; step = the position of the token
+   * whose logits are drawn from (prompt length - 1 at prefill, pos at decode),
+   * sequence = the cache row. */
+  const flexq_gen_config* gen;
+  /* NULL, or device int32 [cache batch]: stopped flag of each cache row, set by
+   * flexq_prefill from the first token and kept by flexq_decode_step (needs a stop
+   * token in gen). */
+  int32_t* stopped;
 } flexq_model;
 
 const char* flexq_status_string(int status);
@@ -257,6 +284,15 @@ int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, int32_t seq,
 /* Greedy pick: next[m] = argmax_n logits[m][n], lowest index among equal maxima. */
 int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next, hipStream_t stream);
 
+/* Next tokens of M sequences from fp32 logits [M][N] under a generation config
+ * (see flexq_gen_config; gen is a HOST pointer, NULL = greedy).  Row m is sequence
+ * m0 + m of generation step `step`; sampling needs 0 <= step < 65536 and
+ * m0 + M <= 65536.  stopped: NULL, or device int32 [M] read and updated in place
+ * (used only with a stop token).  next: device int32 [M].  Errors: bad sizes,
+ * temperature <= 0 or not finite, stop >= N -> FLEXQ_ERR_INVALID. */
+int flexq_pick(const float* logits, int64_t M, int64_t N, const flexq_gen_config* gen,
+               int32_t step, int32_t m0, int32_t* stopped, int32_t* next, hipStream_t stream);
+
 /* One decoder layer, prefill of nb sequences of S tokens: x_out [nb*S][h] from
  * x_in [nb*S][h] (distinct buffers), filling cache rows b0.. positions [0, S). */
 size_t flexq_layer_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, int64_t rows,
@@ -284,7 +320,7 @@ size_t flexq_model_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, in
 int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32_t S, int32_t b0,
                   int32_t* next, float* logits, hipStream_t stream);
 
-/* One greedy decode step of B sequences (cache rows 0..B-1): tokens int32 [B]
+/* One decode step of B sequences (cache rows 0..B-1): tokens int32 [B]
  * at position pos -> next [B] (and logits [B][vocab] if not NULL).  The call
  * neither synchronises nor allocates, so a caller may capture it in a HIP graph
  * (pos is baked into the captured kernels). */
