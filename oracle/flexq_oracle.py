@@ -45,7 +45,11 @@ Readings of the pages where they leave a step open (each also listed in DESIGN.m
     stopped flags): a draw from softmax(logits / T) taken by the Gumbel-max rule in
     float64, its uniforms from SplitMix64 (a counter-based generator, implemented on
     each side from its published definition) keyed by (seed, step, sequence, token);
-    a sequence that produces the stop token is stopped and produces it from then on.
+    a sequence that produces the stop token is stopped and produces it from then on;
+  * ragged prompts ([NOTES] "Flex Opt": the attention_mask buffer of `generate`): prompts
+    are left-padded to a common length; a sequence's pad count is kept with its cache
+    row; attention never sees a pad key (a pad query's output is 0) and positions count
+    from the first real token, so a padded sequence computes what it would alone.
 """
 from __future__ import annotations
 
@@ -305,6 +309,8 @@ class KVCache:
 
     def __init__(self, batch, heads, head_dim, max_len):
         self.batch, self.heads, self.head_dim, self.max_len = batch, heads, head_dim, max_len
+        # left padding of each cache row: positions [0, pad) hold pad tokens, never attended
+        self.pad = np.zeros(batch, np.int64)
         self.k_codes = np.zeros((batch, heads, max_len, head_dim // 2), np.uint8)
         self.v_codes = np.zeros_like(self.k_codes)
         self.k_params = np.zeros((batch, heads, max_len, head_dim // GROUP, 2), F16)
@@ -337,25 +343,32 @@ def _softmax_rows(s):
     return p / p.sum(axis=-1, keepdims=True)
 
 
-def attn_prefill(qkv, batch, seq, heads, head_dim, cache: KVCache | None = None, b0=0):
+def attn_prefill(qkv, batch, seq, heads, head_dim, cache: KVCache | None = None, b0=0, pad=None):
     """Causal attention over the prompt (the pages' `mha`), then 4-bit store of K and V.
 
     qkv: fp16 [batch*seq][3h], rows ordered (b, t).  Returns fp16 [batch*seq][h].
     Scores use the fp16 K/V of this pass; K and V then go to cache rows b0+b, positions [0, seq).
+    Left padding (the pages' attention_mask): sequence b's first pad[b] positions (default:
+    the cache rows' pad, else 0; clamped to [0, seq - 1]) are pad tokens, so query t sees
+    keys pad[b] <= j <= t; a pad query sees none and its output is 0.
     """
     qkv = np.asarray(qkv, dtype=F16).reshape(batch, seq, -1)
     q, k, v = _split_qkv(qkv, heads, head_dim)         # [B][S][nh][hd]
-    out = np.empty((batch, seq, heads, head_dim), F16)
+    out = np.zeros((batch, seq, heads, head_dim), F16)
     scale = 1.0 / np.sqrt(head_dim)
+    if pad is None:
+        pad = cache.pad[b0:b0 + batch] if cache is not None else np.zeros(batch, np.int64)
+    pad = np.clip(np.asarray(pad, np.int64), 0, seq - 1)
     causal = np.tril(np.ones((seq, seq), dtype=bool))
     for b in range(batch):
+        p0 = int(pad[b])
         for hh in range(heads):
-            qh = q[b, :, hh].astype(F64)
-            kh = k[b, :, hh].astype(F64)
-            vh = v[b, :, hh].astype(F64)
+            qh = q[b, p0:, hh].astype(F64)
+            kh = k[b, p0:, hh].astype(F64)
+            vh = v[b, p0:, hh].astype(F64)
             s = (qh @ kh.T) * scale
-            s = np.where(causal, s, -np.inf)
-            out[b, :, hh] = (_softmax_rows(s) @ vh).astype(F16)
+            s = np.where(causal[:seq - p0, :seq - p0], s, -np.inf)
+            out[b, p0:, hh] = (_softmax_rows(s) @ vh).astype(F16)
         if cache is not None:
             cache.store(b0 + b, 0, np.ascontiguousarray(k[b].transpose(1, 0, 2)),
                         np.ascontiguousarray(v[b].transpose(1, 0, 2)))
@@ -366,8 +379,8 @@ def attn_decode(qkv, pos, cache: KVCache, b0=0):
     """One new token per sequence attends to the 4-bit cache (the pages' `mha_gen`).
 
     qkv: fp16 [nb][3h] for cache rows b0..b0+nb-1.  The token's k, v are quantized into
-    position `pos` first; positions [0, pos] are then read back from the 4-bit cache.
-    Returns fp16 [nb][h].
+    position `pos` first; positions [pad, pos] are then read back from the 4-bit cache,
+    pad = the cache row's left padding clamped to [0, pos].  Returns fp16 [nb][h].
     """
     heads, head_dim = cache.heads, cache.head_dim
     qkv = np.asarray(qkv, dtype=F16)
@@ -377,8 +390,10 @@ def attn_decode(qkv, pos, cache: KVCache, b0=0):
     scale = 1.0 / np.sqrt(head_dim)
     for i in range(nb):
         cache.store(b0 + i, pos, k[i][:, None, :], v[i][:, None, :])
+        p0 = int(np.clip(cache.pad[b0 + i], 0, pos))
         for hh in range(heads):
             kh, vh = cache.read(b0 + i, hh, pos + 1)
+            kh, vh = kh[p0:], vh[p0:]
             s = (kh @ q[i, hh].astype(F64)) * scale
             p = _softmax_rows(s[None, :])[0]
             out[i, hh] = (p @ vh).astype(F16)
@@ -518,11 +533,19 @@ class QModel:
     def new_caches(self, batch, max_len):
         return [KVCache(batch, L.heads, L.head_dim, max_len) for L in self.layers]
 
-    def prefill(self, tokens, caches, b0=0):
-        """tokens int [nb][S] -> (logits [nb][V], next token [nb])."""
+    def prefill(self, tokens, caches, b0=0, pad=None):
+        """tokens int [nb][S] -> (logits [nb][V], next token [nb]).
+
+        pad: left padding of each sequence (default 0; clamped to [0, S - 1]), recorded in
+        the caches' rows b0.. for the decode steps.  A token's position counts from its
+        sequence's first real token (pad tokens take position 0)."""
         tokens = np.asarray(tokens)
         nb, seq = tokens.shape
-        positions = np.tile(np.arange(seq), nb)
+        pad = np.zeros(nb, np.int64) if pad is None else np.clip(np.asarray(pad, np.int64), 0,
+                                                                     seq - 1)
+        for c in caches:
+            c.pad[b0:b0 + nb] = pad
+        positions = np.maximum(np.arange(seq)[None, :] - pad[:, None], 0).reshape(-1)
         x = embed(tokens, positions, self.e_codes, self.e_params, self.pos)
         for L, c in zip(self.layers, caches):
             x = L.prefill(x, nb, seq, c, b0)
@@ -532,19 +555,21 @@ class QModel:
     def decode_step(self, tokens, pos, caches, b0=0):
         """tokens int [nb] at position pos -> (logits [nb][V], next token [nb])."""
         tokens = np.asarray(tokens).reshape(-1)
-        x = embed(tokens, np.full(tokens.shape, pos), self.e_codes, self.e_params, self.pos)
+        positions = np.maximum(pos - caches[0].pad[b0:b0 + tokens.size], 0)
+        x = embed(tokens, positions, self.e_codes, self.e_params, self.pos)
         for L, c in zip(self.layers, caches):
             x = L.decode(x, pos, c, b0)
         return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
-    def generate(self, tokens, gen, config=None):
+    def generate(self, tokens, gen, config=None, pad=None):
         """Generation of `gen` tokens ([WALK] section 4.1): greedy without `config`, else
-        `pick` with it (do_sample, temperature, seed, stop)."""
+        `pick` with it (do_sample, temperature, seed, stop); `pad` = left padding of each
+        prompt (the attention mask of a ragged batch)."""
         tokens = np.asarray(tokens)
         nb, seq = tokens.shape
         caches = self.new_caches(nb, seq + gen - 1)
         stopped = np.zeros(nb, dtype=bool)
-        lg, nxt = self.prefill(tokens, caches)
+        lg, nxt = self.prefill(tokens, caches, pad=pad)
         if config is not None:
             nxt = pick(lg, config, seq - 1, 0, stopped)
         out = [nxt]
