@@ -15,6 +15,9 @@
 //  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs;
 //  5. with several splits, each writes (max, sum, o[]) and a merge kernel rescales
 //     and adds them in split order.
+// Left padding: positions below the sequence's pad count are never read; a split that
+// lies wholly below it writes an empty partial (max -inf, sum 0), which the merge
+// weights by 0 (the split holding pos is never empty).
 #include <algorithm>
 
 #include "quant_dev.h"
@@ -37,8 +40,9 @@ __device__ __forceinline__ float byte_f(uint32_t w) { return (float)((w >> (8 * 
 
 template <int HD, int UNR>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict__ qkv, int b0,
-                                                          int pos, KVViewD kv, int chunk,
-                                                          f16* __restrict__ out,
+                                                          int pos, KVViewD kv,
+                                                          const int32_t* __restrict__ pad,
+                                                          int chunk, f16* __restrict__ out,
                                                           float* __restrict__ part,
                                                           float scale_log2) {
   constexpr int LPT = HD / 32;     // lanes per token
@@ -55,8 +59,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   const int nh = kv.nh;
   const int h = nh * HD;
   const int T = pos + 1;
-  const int t_begin = split * chunk;
-  const int t_end = min(T, t_begin + chunk);
+  const int t_end = min(T, split * chunk + chunk);
+  const int npad = pad ? min(max(pad[b0 + bi], 0), pos) : 0;
+  const int t_begin = max(split * chunk, npad);
   const f16* row = qkv + (int64_t)bi * 3 * h;
   const int64_t slot0 = ((int64_t)(b0 + bi) * nh + head) * kv.max_len;
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   __syncthreads();
 
   // ---- 3. softmax statistics of this split
-  const int n = t_end - t_begin;
+  const int n = t_end - t_begin;   // <= 0 for a split wholly in the padding
   float mx = -INFINITY;
   for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
   mx = wave_max(mx);
@@ -277,21 +282,21 @@ static DecPlan dec_plan(int B, int heads, int head_dim, int pos) {
 
 template <int HD, int UNR>
 static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
-                       const KVViewD& v, f16* out, float* ws, float scale_log2,
-                       hipStream_t stream) {
+                       const KVViewD& v, const int32_t* pad, f16* out, float* ws,
+                       float scale_log2, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_kernel<HD, UNR>), grid, dim3(256), 0, stream, qkv, b0, pos, v,
-                     p.chunk, out, ws, scale_log2);
+                     pad, p.chunk, out, ws, scale_log2);
 }
 
 template <int HD>
 static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
-                       const KVViewD& v, f16* out, float* ws, float scale_log2,
-                       hipStream_t stream) {
+                       const KVViewD& v, const int32_t* pad, f16* out, float* ws,
+                       float scale_log2, hipStream_t stream) {
   switch (p.unr) {
-    case 4: launch_dec<HD, 4>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
-    case 3: launch_dec<HD, 3>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
-    case 2: launch_dec<HD, 2>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
-    default: launch_dec<HD, 1>(p, grid, qkv, b0, pos, v, out, ws, scale_log2, stream); break;
+    case 4: launch_dec<HD, 4>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
+    case 3: launch_dec<HD, 3>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
+    case 2: launch_dec<HD, 2>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
+    default: launch_dec<HD, 1>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
   }
 }
 
@@ -317,7 +322,8 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   if (kv->heads <= 0 || b0 + B > kv->batch || pos >= kv->max_len) return FLEXQ_ERR_INVALID;
   if (!kv->k_codes || !kv->v_codes || !kv->k_params || !kv->v_params) return FLEXQ_ERR_INVALID;
   if (((uintptr_t)qkv & 15) || ((uintptr_t)out & 1) || ((uintptr_t)kv->k_codes & 15) ||
-      ((uintptr_t)kv->v_codes & 15) || ((uintptr_t)kv->k_params & 3) || ((uintptr_t)kv->v_params & 3))
+      ((uintptr_t)kv->v_codes & 15) || ((uintptr_t)kv->k_params & 3) || ((uintptr_t)kv->v_params & 3) ||
+      ((uintptr_t)kv->pad & 3))
     return FLEXQ_ERR_INVALID;
   if (kv->heads > 65535 || B > 65535) return FLEXQ_ERR_UNSUPPORTED;
   const DecPlan p = dec_plan(B, kv->heads, kv->head_dim, pos);
@@ -328,12 +334,14 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
   dim3 grid(p.splits, kv->heads, B);
   if (kv->head_dim == 64) {
-    launch_dec<64>(p, grid, (const f16*)qkv, b0, pos, v, (f16*)out, (float*)ws, scale_log2, stream);
+    launch_dec<64>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, (float*)ws,
+                   scale_log2, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(kv->heads, B), dim3(64), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);
   } else {
-    launch_dec<128>(p, grid, (const f16*)qkv, b0, pos, v, (f16*)out, (float*)ws, scale_log2, stream);
+    launch_dec<128>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, (float*)ws,
+                    scale_log2, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(kv->heads, B), dim3(128), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);

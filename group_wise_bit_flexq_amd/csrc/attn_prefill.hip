@@ -22,6 +22,9 @@
 //    dim i of the 4 keys.
 // After the loop the work-group quantizes K and V of its own 128 positions into the
 // cache (4 lanes per 64-element group), reading them from the staged LDS tiles.
+// Left padding (the generation loop's attention mask): keys below the sequence's pad
+// count are masked, key blocks wholly below it are skipped (except the work-group's
+// own two, which the store needs staged), and a query with no visible key writes 0.
 #include "quant_dev.h"
 
 namespace flexq {
@@ -61,6 +64,7 @@ __device__ __forceinline__ int k_off(int row, int ch) {
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restrict__ qkv, int S,
                                                            int nh, int b0, KVView kv,
+                                                           const int32_t* __restrict__ pad,
                                                            f16* __restrict__ out,
                                                            float scale_log2) {
   using P = PrefillShape<HD>;
@@ -93,8 +97,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   const int hl = lane >> 5;                // lane half
   const int qabs = wq0 + (lane & 31);
   const int qrow = min(qabs, S - 1);
-  const int kend = min(q0 + QB, S);        // keys this work-group needs: [0, kend)
+  const int kend = min(q0 + QB, S);        // keys this work-group needs: [pb, kend)
   const int nkb = (kend + KB - 1) / KB;
+  const int pb = pad ? min(max(pad[b0 + b], 0), S - 1) : 0;
+  const int kb0 = min(pb / KB, 2 * qb);    // the own blocks 2 qb, 2 qb + 1 stay staged
 
   // Q^T operand: lane (q, half) holds Q[q][16 ks + 8 half .. +7]
   f16x8 qf[KS];
@@ -136,14 +142,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   const int tr_key = 4 * hl + (tr_i >> 2);
   const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
 
-  LOAD_KV(0);
-  for (int kb = 0; kb < nkb; ++kb) {
+  LOAD_KV(kb0);
+  for (int kb = kb0; kb < nkb; ++kb) {
     const int st = kb & 1;
     STORE_KV(st);
     if (kb + 1 < nkb) LOAD_KV(kb + 1);
     __syncthreads();
     const int k0 = kb * KB;
-    if (k0 <= wq0 + 31) {   // some key of the block is visible to some query of the wave
+    // some key of the block is visible to some query of the wave
+    if (k0 <= wq0 + 31 && k0 + KB > pb && wq0 + 31 >= pb) {
       const f16* sk = sK + st * P::K_STAGE;
       const f16* sv = sV + st * P::V_STAGE;
       f32x16 s[2];
@@ -169,6 +176,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
           for (int r = 0; r < 16; ++r)
             if (32 * t + 8 * (r >> 2) + (r & 3) > lim) s[t][r] = -INFINITY;
       }
+      if (k0 < pb) {   // the block holds pad keys
+        const int lo = pb - k0 - 4 * hl;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) < lo) s[t][r] = -INFINITY;
+      }
       float mb = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -181,12 +196,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
       const bool grow = mb > m_run + 8.0f;
       if (__builtin_amdgcn_ballot_w64(grow)) {   // wave-uniform branch
         const float m_new = grow ? mb : m_run;
-        const float alpha = exp2f(m_run - m_new);  // m_run = -inf on the first block -> 0
+        // m_run = -inf on the first block -> 0; lanes that keep their reference take 1
+        // (also a pad query's, whose m_run stays -inf)
+        const float alpha = grow ? exp2f(m_run - m_new) : 1.0f;
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DT; ++i) o[i] *= alpha;
         m_run = m_new;
       }
+      // a query that has seen no visible key yet (a pad query) keeps m_run = -inf:
+      // its masked scores then give p = 2^-inf = 0 instead of 2^(-inf + inf)
+      const float m_ref = m_run == -INFINITY ? 0.0f : m_run;
       float ls = 0.0f;
       f16x8 pf[4];
 #pragma unroll
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           // v_exp_f32: results below 2^-126 flush to 0 (they vanish in the fp16 P anyway)
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], scale_log2, -m_run));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], scale_log2, -m_ref));
           ls += p;
           pf[2 * t + (r >> 3)][r & 7] = (f16)p;
         }
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
 
   // O^T lane l reg r = dim 32 dt + 8 (r / 4) + 4 (l / 32) + r % 4 of query l % 32
   if (qabs < S) {
-    const float inv = 1.0f / l_run;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;   // 0 for a pad query
     f16* orow = out + ((int64_t)b * S + qabs) * h + head * HD;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -291,7 +311,8 @@ extern "C" int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int
   if (kv->heads <= 0 || b0 + B > kv->batch || S > kv->max_len) return FLEXQ_ERR_INVALID;
   if (!kv->k_codes || !kv->v_codes || !kv->k_params || !kv->v_params) return FLEXQ_ERR_INVALID;
   if (((uintptr_t)qkv & 15) || ((uintptr_t)out & 15) || ((uintptr_t)kv->k_codes & 15) ||
-      ((uintptr_t)kv->v_codes & 15) || ((uintptr_t)kv->k_params & 3) || ((uintptr_t)kv->v_params & 3))
+      ((uintptr_t)kv->v_codes & 15) || ((uintptr_t)kv->k_params & 3) || ((uintptr_t)kv->v_params & 3) ||
+      ((uintptr_t)kv->pad & 3))
     return FLEXQ_ERR_INVALID;
   if (kv->heads > 65535 || B > 65535) return FLEXQ_ERR_UNSUPPORTED;
   KVView v{kv->k_codes, kv->v_codes, (uint32_t*)kv->k_params, (uint32_t*)kv->v_params, kv->heads,
@@ -309,10 +330,11 @@ extern "C" int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int
   }
   if (kv->head_dim == 64)
     hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), PrefillShape<64>::LDS_BYTES, stream,
-                       (const f16*)qkv, S, kv->heads, b0, v, (f16*)out, scale_log2);
+                       (const f16*)qkv, S, kv->heads, b0, v, kv->pad, (f16*)out, scale_log2);
   else
     hipLaunchKernelGGL(attn_prefill_kernel<128>, grid, dim3(256), PrefillShape<128>::LDS_BYTES,
-                       stream, (const f16*)qkv, S, kv->heads, b0, v, (f16*)out, scale_log2);
+                       stream, (const f16*)qkv, S, kv->heads, b0, v, kv->pad, (f16*)out,
+                       scale_log2);
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
 }

@@ -68,10 +68,12 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const f16* __rest
   }
 }
 
-// out[m][k] = fp16(fp16(c * s + off) + pos[p + 2][k]) with p = pos_base + m % seq.
-// One work-group per row, 16 elements per thread and step.
+// out[m][k] = fp16(fp16(c * s + off) + pos[p + 2][k]) with p = pos_base + m % seq
+// - pad[m / seq] (left padding; p >= 0).  One work-group per row, 16 elements per
+// thread and step.
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
-                                                    int pos_base, int seq, int h,
+                                                    int pos_base, int seq,
+                                                    const int32_t* __restrict__ pad, int h,
                                                     const uint2* __restrict__ codes,
                                                     const uint32_t* __restrict__ params,
                                                     const f16* __restrict__ pos, int pos_rows,
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   const int64_t m = blockIdx.x;
   int tok = tokens[m];
   tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
-  int p = pos_base + (int)(m % seq) + 2;
+  int p = pos_base + (int)(m % seq) - (pad ? pad[m / seq] : 0);
+  p = (p < 0 ? 0 : p) + 2;
   p = p >= pos_rows ? pos_rows - 1 : p;
   const int KT = h / 64;
   for (int c = threadIdx.x; c < h / 16; c += blockDim.x) {
@@ -227,8 +230,8 @@ extern "C" int flexq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64_t 
 }
 
 extern "C" int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, int32_t seq,
-                           const flexq_w4* embed, const uint16_t* pos, int32_t pos_rows,
-                           uint16_t* out, hipStream_t stream) {
+                           const int32_t* pad, const flexq_w4* embed, const uint16_t* pos,
+                           int32_t pos_rows, uint16_t* out, hipStream_t stream) {
   if (n < 0 || !embed || seq <= 0 || pos_base < 0) return FLEXQ_ERR_INVALID;
   if (n == 0) return FLEXQ_OK;
   if (!tokens || !embed->codes || !embed->params || !pos || !out) return FLEXQ_ERR_INVALID;
@@ -236,11 +239,11 @@ extern "C" int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, i
   if (h <= 0 || h % 64 || embed->rows <= 0) return FLEXQ_ERR_INVALID;
   if ((int64_t)pos_base + (n < seq ? n : seq) - 1 + 2 >= pos_rows) return FLEXQ_ERR_INVALID;
   if (((uintptr_t)embed->codes & 7) || ((uintptr_t)embed->params & 3) || ((uintptr_t)pos & 15) ||
-      ((uintptr_t)out & 15))
+      ((uintptr_t)out & 15) || ((uintptr_t)pad & 3))
     return FLEXQ_ERR_INVALID;
   if (n > 0x7FFFFFFF || embed->rows > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(embed_kernel, dim3((unsigned)n), dim3(256), 0, stream, tokens, pos_base, seq,
-                     (int)h, (const uint2*)embed->codes, (const uint32_t*)embed->params,
+                     pad, (int)h, (const uint2*)embed->codes, (const uint32_t*)embed->params,
                      (const f16*)pos, pos_rows, (int)embed->rows, (f16*)out);
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;

@@ -237,10 +237,14 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
   TRY(check_model(m));
   if (nb < 0 || S < 0 || b0 < 0 || !tokens || !next) return FLEXQ_ERR_INVALID;
   if (nb == 0 || S == 0) return FLEXQ_OK;
+  // cache rows (pad counts and stopped flags are indexed by them before any layer runs)
+  if ((int64_t)b0 + nb > m->kv[0].batch || S > m->kv[0].max_len) return FLEXQ_ERR_INVALID;
   const int64_t rows = (int64_t)nb * S;
   ModelScratch s;
   TRY(model_scratch(m, rows, nb, 0, &s));
-  TRY(flexq_embed(tokens, rows, 0, S, &m->embed, m->pos, m->pos_rows, s.x0, stream));
+  const int32_t* pad = m->kv[0].pad;
+  TRY(flexq_embed(tokens, rows, 0, S, pad ? pad + b0 : nullptr, &m->embed, m->pos, m->pos_rows,
+                  s.x0, stream));
   LayerScratch ls;
   layer_carve(s.layer_base, m->hidden, m->heads, m->ffn, rows, 0, &ls);
   uint16_t* x = s.x0;
@@ -260,9 +264,11 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
   TRY(check_model(m));
   if (B < 0 || pos < 0 || !tokens || !next) return FLEXQ_ERR_INVALID;
   if (B == 0) return FLEXQ_OK;
+  if (B > m->kv[0].batch || pos >= m->kv[0].max_len) return FLEXQ_ERR_INVALID;
   ModelScratch s;
   TRY(model_scratch(m, B, B, pos + 1, &s));
-  TRY(flexq_embed(tokens, B, pos, 1, &m->embed, m->pos, m->pos_rows, s.x0, stream));
+  TRY(flexq_embed(tokens, B, pos, 1, m->kv[0].pad, &m->embed, m->pos, m->pos_rows, s.x0,
+                  stream));
   LayerScratch ls;
   layer_carve(s.layer_base, m->hidden, m->heads, m->ffn, B, pos + 1, &ls);
   uint16_t* x = s.x0;

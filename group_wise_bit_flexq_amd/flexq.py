@@ -46,7 +46,7 @@ class W4Struct(C.Structure):
 class KV4Struct(C.Structure):
     _fields_ = [("k_codes", C.c_void_p), ("v_codes", C.c_void_p), ("k_params", C.c_void_p),
                 ("v_params", C.c_void_p), ("batch", C.c_int32), ("heads", C.c_int32),
-                ("head_dim", C.c_int32), ("max_len", C.c_int32)]
+                ("head_dim", C.c_int32), ("max_len", C.c_int32), ("pad", C.c_void_p)]
 
 
 class LayerStruct(C.Structure):
@@ -105,7 +105,8 @@ def lib():
             "flexq_attn_decode_workspace_size": (sz, [i32, i32, i32, i32]),
             "flexq_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct), vp, vp,
                                                 sz, vp]),
-            "flexq_embed": (C.c_int, [vp, i64, i32, i32, C.POINTER(W4Struct), vp, i32, vp, vp]),
+            "flexq_embed": (C.c_int, [vp, i64, i32, i32, vp, C.POINTER(W4Struct), vp, i32, vp,
+                                      vp]),
             "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
             "flexq_pick": (C.c_int, [vp, i64, i64, C.POINTER(GenConfig), i32, i32, vp, vp, vp]),
             "flexq_layer_workspace_size": (sz, [i32, i32, i32, i64, i32]),
@@ -209,10 +210,16 @@ class W4:
 
 
 class KV4:
-    """The 4-bit KV cache of one layer (see flexq_kv4_layer)."""
+    """The 4-bit KV cache of one layer (see flexq_kv4_layer); `pad` is None or a device
+    int32 [batch] tensor of left-padding counts."""
 
-    def __init__(self, batch, heads, head_dim, max_len, device="cuda"):
+    def __init__(self, batch, heads, head_dim, max_len, device="cuda", pad=None):
         self.batch, self.heads, self.head_dim, self.max_len = batch, heads, head_dim, max_len
+        if pad is not None:
+            _need(pad, torch.int32, "pad")
+            if pad.numel() != batch:
+                raise ValueError("pad: one entry per cache row")
+        self.pad = pad
         shp = (batch, heads, max_len, head_dim // 2)
         pshp = (batch, heads, max_len, head_dim // 64, 2)
         self.k_codes = torch.zeros(shp, dtype=torch.uint8, device=device)
@@ -223,7 +230,7 @@ class KV4:
     def c(self) -> KV4Struct:
         return KV4Struct(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
                          self.k_params.data_ptr(), self.v_params.data_ptr(), self.batch,
-                         self.heads, self.head_dim, self.max_len)
+                         self.heads, self.head_dim, self.max_len, _ptr(self.pad))
 
     def nbytes(self):
         return 2 * (self.k_codes.numel() + self.k_params.numel() * 2)
@@ -386,13 +393,16 @@ def attn_decode(qkv, pos, kv: KV4, b0=0, out=None, ws=None, stream=None):
     return y
 
 
-def embed(tokens, pos_base, seq, emb: W4, pos_table, out=None, stream=None):
+def embed(tokens, pos_base, seq, emb: W4, pos_table, out=None, stream=None, pad=None):
     _need(tokens, torch.int32, "tokens")
     n = tokens.numel()
     y = out if out is not None else torch.empty(n, emb.cols, dtype=torch.float16,
                                                 device=tokens.device)
+    if pad is not None:
+        _need(pad, torch.int32, "pad")
     ec = emb.c()
-    _check("flexq_embed", lib().flexq_embed(tokens.data_ptr(), n, pos_base, seq, C.byref(ec),
+    _check("flexq_embed", lib().flexq_embed(tokens.data_ptr(), n, pos_base, seq, _ptr(pad),
+                                            C.byref(ec),
                                             pos_table.data_ptr(), pos_table.shape[0],
                                             y.data_ptr(), _stream(stream)))
     return y
@@ -503,7 +513,9 @@ class QModel:
         self.ffn = layers[0].ffn
         self.batch, self.max_len = batch, max_len
         hd = self.hidden // heads
-        self.caches = [KV4(batch, heads, hd, max_len, device) for _ in layers]
+        # left padding of each cache row, shared by every layer's cache (0: none)
+        self.pad = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.caches = [KV4(batch, heads, hd, max_len, device, pad=self.pad) for _ in layers]
         nbytes = lib().flexq_model_workspace_size(self.hidden, heads, self.ffn, self.vocab,
                                                   max_prefill_rows, batch, max_len)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -524,9 +536,17 @@ class QModel:
             self.stopped = torch.zeros(self.batch, dtype=torch.int32, device=self.workspace.device)
         self._struct.stopped = _ptr(self.stopped)
 
-    def prefill(self, tokens, b0=0, logits=None, next_out=None, stream=None):
+    def prefill(self, tokens, b0=0, logits=None, next_out=None, stream=None, pad=None):
+        """Prefill of cache rows b0.. from tokens [nb][S]; `pad` (None or nb ints): left
+        padding of each ragged prompt, recorded for the later decode steps."""
         _need(tokens, torch.int32, "tokens")
         nb, S = tokens.shape
+        if b0 < 0 or b0 + nb > self.batch:
+            raise ValueError("prefill rows outside the cache")
+        if pad is None:
+            self.pad[b0:b0 + nb].zero_()
+        else:
+            self.pad[b0:b0 + nb].copy_(torch.as_tensor(pad, dtype=torch.int32).reshape(nb))
         nxt = next_out if next_out is not None else torch.empty(nb, dtype=torch.int32,
                                                                 device=tokens.device)
         _need(nxt, torch.int32, "next_out")

@@ -83,7 +83,14 @@ typedef struct {
 /* The 4-bit KV cache of one layer.  Groups are 64 consecutive head_dim elements
  * of one token's K (or V) vector in one head.
  *   k_codes, v_codes   [batch][heads][max_len][head_dim/2]
- *   k_params, v_params [batch][heads][max_len][head_dim/64][2]      */
+ *   k_params, v_params [batch][heads][max_len][head_dim/64][2]
+ *   pad                NULL, or device int32 [batch]: left padding of each cache row
+ *                      (ragged prompts; source notes "Flex Opt", the attention mask of
+ *                      generate).  Positions [0, pad) of the row hold pad tokens:
+ *                      attention never reads them, and a pad query's prefill output is
+ *                      0.  Valid values lie in [0, prompt length); others are clamped
+ *                      to [0, S - 1] at prefill and [0, pos] at decode.  Read by the
+ *                      kernels when they run, so it may change between calls. */
 typedef struct {
   uint8_t* k_codes;
   uint8_t* v_codes;
@@ -93,6 +100,7 @@ typedef struct {
   int32_t heads;
   int32_t head_dim; /* 64 or 128 */
   int32_t max_len;
+  const int32_t* pad;
 } flexq_kv4_layer;
 
 /* Weights of one pre-LayerNorm OPT decoder layer (source notes, "Flex Opt": the
@@ -274,12 +282,14 @@ int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t po
 /* ---------------------------------------------------------------- model pieces
  * Token + position embedding (`opt_input_embed`, source notes "Pytorch Backend"):
  * out[m] = fp16(dequant(embed row tokens[m]) + pos[p + 2]) with position
- * p = pos_base + m % seq (prefill: pos_base 0, seq S; decode: pos_base = pos,
- * seq 1).  tokens: device int32 [n], ids outside [0, vocab) are clamped.
+ * p = max(pos_base + m % seq - pad[m / seq], 0) (prefill: pos_base 0, seq S; decode:
+ * pos_base = pos, seq 1).  pad: NULL (no padding) or device int32 [n / seq], the
+ * left padding of each sequence, so positions count from its first real token.
+ * tokens: device int32 [n], ids outside [0, vocab) are clamped.
  * pos_base + min(n, seq) - 1 + 2 must be < pos_rows. */
 int flexq_embed(const int32_t* tokens, int64_t n, int32_t pos_base, int32_t seq,
-                const flexq_w4* embed, const uint16_t* pos, int32_t pos_rows, uint16_t* out,
-                hipStream_t stream);
+                const int32_t* pad, const flexq_w4* embed, const uint16_t* pos,
+                int32_t pos_rows, uint16_t* out, hipStream_t stream);
 
 /* Greedy pick: next[m] = argmax_n logits[m][n], lowest index among equal maxima. */
 int flexq_argmax(const float* logits, int64_t M, int64_t N, int32_t* next, hipStream_t stream);
@@ -314,7 +324,10 @@ size_t flexq_model_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, in
                                   int64_t max_prefill_rows, int32_t max_batch, int32_t max_len);
 
 /* Prefill of one micro-batch (source notes, "Flex Opt": embedding, layers, output
- * head): tokens int32 [nb][S] for cache rows b0..b0+nb-1.  Writes the first
+ * head): tokens int32 [nb][S] for cache rows b0..b0+nb-1.  Ragged prompts are
+ * left-padded to S; the pad counts are kv[0].pad (every layer's kv must point at
+ * the same array, rows b0.. written before the call), used for the positions and
+ * by every layer's attention.  Writes the first
  * generated token of each sequence to next [nb] and, if logits != NULL, the fp32
  * logits of the last prompt position to logits [nb][vocab]. */
 int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32_t S, int32_t b0,
