@@ -46,6 +46,10 @@ Readings of the pages where they leave a step open (each also listed in DESIGN.m
     float64, its uniforms from SplitMix64 (a counter-based generator, implemented on
     each side from its published definition) keyed by (seed, step, sequence, token);
     a sequence that produces the stop token is stopped and produces it from then on;
+  * attention sparsity ([NOTES] "Flex Opt": the attn_sparsity policy, no mechanism
+    given): in decode attention each query keeps its ceil(n * sparsity) highest scores
+    (lower position first on equal scores) and takes the softmax over those alone;
+    prefill attention stays dense;
   * ragged prompts ([NOTES] "Flex Opt": the attention_mask buffer of `generate`): prompts
     are left-padded to a common length; a sequence's pad count is kept with its cache
     row; attention never sees a pad key (a pad query's output is 0) and positions count
@@ -375,12 +379,23 @@ def attn_prefill(qkv, batch, seq, heads, head_dim, cache: KVCache | None = None,
     return out.reshape(batch * seq, heads * head_dim)
 
 
-def attn_decode(qkv, pos, cache: KVCache, b0=0):
+def topk_count(sparsity, n):
+    """Positions kept by sparse attention over n candidates: k = ceil(sparsity * n), the
+    product taken in float32 (sparsity a float32), at least 1 and at most n."""
+    k = int(np.ceil(np.float32(sparsity) * np.float32(n)))
+    return min(max(k, 1), n)
+
+
+def attn_decode(qkv, pos, cache: KVCache, b0=0, sparsity=1.0):
     """One new token per sequence attends to the 4-bit cache (the pages' `mha_gen`).
 
     qkv: fp16 [nb][3h] for cache rows b0..b0+nb-1.  The token's k, v are quantized into
     position `pos` first; positions [pad, pos] are then read back from the 4-bit cache,
     pad = the cache row's left padding clamped to [0, pos].  Returns fp16 [nb][h].
+    sparsity < 1 ([NOTES] "Flex Opt": the attn_sparsity policy): each query keeps only
+    its k = topk_count(sparsity, n) highest-scoring positions of the n candidates (the
+    lower position first among equal scores) and attends to them alone (softmax over
+    the kept scores).
     """
     heads, head_dim = cache.heads, cache.head_dim
     qkv = np.asarray(qkv, dtype=F16)
@@ -395,6 +410,10 @@ def attn_decode(qkv, pos, cache: KVCache, b0=0):
             kh, vh = cache.read(b0 + i, hh, pos + 1)
             kh, vh = kh[p0:], vh[p0:]
             s = (kh @ q[i, hh].astype(F64)) * scale
+            kept = topk_count(sparsity, s.size)
+            if kept < s.size:
+                keep = np.lexsort((np.arange(s.size), -s))[:kept]   # by score, then position
+                s, vh = s[keep], vh[keep]
             p = _softmax_rows(s[None, :])[0]
             out[i, hh] = (p @ vh).astype(F16)
     return out.reshape(nb, heads * head_dim)
@@ -431,9 +450,9 @@ class QLayer:
                                                           self.head_dim, cache, b0))
         return self._mlp_block(x1)
 
-    def decode(self, x, pos, cache, b0=0):
+    def decode(self, x, pos, cache, b0=0, sparsity=1.0):
         """x fp16 [nb][h] (one token per sequence at position pos) -> fp16 [nb][h]."""
-        x1 = self._attn_block(x, lambda qkv: attn_decode(qkv, pos, cache, b0))
+        x1 = self._attn_block(x, lambda qkv: attn_decode(qkv, pos, cache, b0, sparsity))
         return self._mlp_block(x1)
 
 
@@ -552,13 +571,13 @@ class QModel:
         last = x.reshape(nb, seq, -1)[:, -1]
         return lm_head(last, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
-    def decode_step(self, tokens, pos, caches, b0=0):
+    def decode_step(self, tokens, pos, caches, b0=0, sparsity=1.0):
         """tokens int [nb] at position pos -> (logits [nb][V], next token [nb])."""
         tokens = np.asarray(tokens).reshape(-1)
         positions = np.maximum(pos - caches[0].pad[b0:b0 + tokens.size], 0)
         x = embed(tokens, positions, self.e_codes, self.e_params, self.pos)
         for L, c in zip(self.layers, caches):
-            x = L.decode(x, pos, c, b0)
+            x = L.decode(x, pos, c, b0, sparsity)
         return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
     def generate(self, tokens, gen, config=None, pad=None):
