@@ -18,7 +18,12 @@
 // Left padding: positions below the sequence's pad count are never read; a split that
 // lies wholly below it writes an empty partial (max -inf, sum 0), which the merge
 // weights by 0 (the split holding pos is never empty).
+// Sparse variant (TOPK, one split per sequence and head): after the K pass the n scores
+// in LDS are cut to the k = ceil(sparsity * n) largest (a 4-pass radix select over
+// order-preserving 32-bit keys, equal keys ranked by position), the others become
+// -inf, and the V pass walks a compacted list of the kept positions only.
 #include <algorithm>
+#include <type_traits>
 
 #include "quant_dev.h"
 
@@ -34,22 +39,139 @@ struct KVViewD {
 
 constexpr int kDecMaxChunk = 4096;  // tokens of one split (scores live in LDS)
 
+// Float -> uint32 with the same order (negative values reversed below the positives).
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Keep the kk largest of sc[0, n) (kk < n; lower index first among equal values) and
+// set the others to -inf.  All 256 threads of the work-group call it; it ends with a
+// barrier.
+__device__ void topk_mask(float* sc, int n, int kk) {
+  __shared__ uint32_t hist[256];
+  __shared__ int pick[3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  int need = kk;  // rank from the top, among keys that match the prefix, of the threshold
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    if (shift == 24) {
+      // the top byte is the sign and most of the exponent: the scores of one query share
+      // a handful of values, so each wave adds one count per distinct bin (a leader
+      // lane per bin) instead of 64 colliding atomics
+      for (int c = 0; c < n; c += 256) {
+        const int i = c + tid;
+        const bool valid = i < n;
+        const uint32_t bin = valid ? ord_key(sc[i]) >> 24 : 0u;
+        uint64_t todo = __ballot(valid);
+        while (todo) {
+          const int leader = __ffsll((long long)todo) - 1;
+          const uint32_t lb = __shfl(bin, leader, 64);
+          const uint64_t same = __ballot(valid && bin == lb) & todo;
+          if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+          todo &= ~same;
+        }
+      }
+    } else {
+      for (int i = tid; i < n; i += 256) {
+        const uint32_t key = ord_key(sc[i]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 255 - 4l .. 252 - 4l (largest first); counts above a lane
+      // come from an exclusive scan over the lanes
+      const int d0 = 255 - 4 * lane;
+      const int c0 = (int)hist[d0], c1 = (int)hist[d0 - 1], c2 = (int)hist[d0 - 2],
+                c3 = (int)hist[d0 - 3];
+      const int tot = c0 + c1 + c2 + c3;
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int above = incl - tot;
+      if (above < need && need <= incl) {
+        int d = d0, c = c0;
+        if (above + c0 < need) {
+          above += c0; d = d0 - 1; c = c1;
+          if (above + c1 < need) {
+            above += c1; d = d0 - 2; c = c2;
+            if (above + c2 < need) { above += c2; d = d0 - 3; c = c3; }
+          }
+        }
+        pick[0] = d;
+        pick[1] = need - above;
+        pick[2] = c;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)pick[0] << shift;
+    pmask |= 255u << shift;
+    need = pick[1];
+    // every key in the chosen bin is kept: the digits so far already decide the cut
+    if (need == pick[2]) break;
+  }
+  // keys whose digits so far exceed the prefix stay; of those equal to it, `need` of
+  // pick[2] stay (all of them after an early exit, else the lowest positions)
+  const uint32_t thr = prefix;
+  const bool all_equal_kept = need == pick[2];
+  for (int i = tid; i < n; i += 256)
+    if ((ord_key(sc[i]) & pmask) < thr) sc[i] = -INFINITY;
+  __syncthreads();
+  if (!all_equal_kept && wave == 0) {   // rank equal keys by position
+    int run = 0;
+    for (int c = 0; c < n; c += 64) {
+      const int i = c + lane;
+      const bool e = i < n && sc[i] != -INFINITY && (ord_key(sc[i]) & pmask) == thr;
+      const uint64_t bal = __ballot(e);
+      const int rank = run + __popcll(bal & ((1ull << lane) - 1ull));
+      if (e && rank >= need) sc[i] = -INFINITY;
+      run += __popcll(bal);
+    }
+  }
+  __syncthreads();
+}
+
+// Indices (into sc) of the entries topk_mask kept, in increasing order, into list;
+// wave 0 walks the scores in 64-wide chunks (ballot + prefix count).  Ends with a
+// barrier.
+__device__ void topk_compact(const float* sc, int n, uint16_t* list) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    int run = 0;
+    for (int c = 0; c < n; c += 64) {
+      const int i = c + lane;
+      const bool keep = i < n && sc[i] != -INFINITY;
+      const uint64_t bal = __ballot(keep);
+      if (keep) list[run + __popcll(bal & ((1ull << lane) - 1ull))] = (uint16_t)i;
+      run += __popcll(bal);
+    }
+  }
+  __syncthreads();
+}
+
 // byte N of a word as float (one v_cvt_f32_ubyteN)
 template <int N>
 __device__ __forceinline__ float byte_f(uint32_t w) { return (float)((w >> (8 * N)) & 0xFFu); }
 
-template <int HD, int UNR>
+template <int HD, int UNR, bool TOPK>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict__ qkv, int b0,
                                                           int pos, KVViewD kv,
                                                           const int32_t* __restrict__ pad,
                                                           int chunk, f16* __restrict__ out,
                                                           float* __restrict__ part,
-                                                          float scale_log2) {
+                                                          float scale_log2, float sparsity) {
   constexpr int LPT = HD / 32;     // lanes per token
   constexpr int TPW = 64 / LPT;    // tokens per wave step
   constexpr int TPB = 4 * TPW;     // tokens per block step
   constexpr int GPT = HD / 64;     // quantization groups per token vector
-  __shared__ float sc[kDecMaxChunk];
+  // dynamic LDS: the split's scores (chunk floats), then for top-k the kept list
+  extern __shared__ __attribute__((aligned(16))) float sc[];
   __shared__ float red[4][HD + LPT];
   __shared__ float wred[8];
 
@@ -144,8 +266,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   }
   __syncthreads();
 
-  // ---- 3. softmax statistics of this split
   const int n = t_end - t_begin;   // <= 0 for a split wholly in the padding
+  // V pass positions: t_begin + j for j < cnt, or t_begin + list[j] for a top-k cut
+  int cnt = n;
+  bool use_list = false;
+  uint16_t* const list = (uint16_t*)(sc + chunk);
+  if constexpr (TOPK) {            // one split: n >= 1 candidates
+    const int kk = max((int)ceilf(fminf(sparsity, 1.0f) * (float)n), 1);
+    if (kk < n) {
+      topk_mask(sc, n, kk);
+      topk_compact(sc, n, list);
+      cnt = kk;
+      use_list = true;
+    }
+  }
+
+  // ---- 3. softmax statistics of this split
   float mx = -INFINITY;
   for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
   mx = wave_max(mx);
@@ -164,43 +300,55 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   __syncthreads();
   const float lsum = (wred[4] + wred[5]) + (wred[6] + wred[7]);
 
-  // ---- 4. V pass
+  // ---- 4. V pass (instantiated with and without the kept list)
   float acc[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float pm = 0.0f;
-  for (int tb = t_begin; tb < t_end; tb += UNR * TPB) {
-    uint4 cw[UNR];
-    uint32_t prm[UNR];
+  auto v_pass = [&](auto with_list) {
+    constexpr bool LIST = decltype(with_list)::value;
+    for (int jb = 0; jb < cnt; jb += UNR * TPB) {
+      uint4 cw[UNR];
+      uint32_t prm[UNR];
+      int rel[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
-      cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
-      prm[u] = kv.vp[(slot0 + t) * GPT + grp];
-    }
+      for (int u = 0; u < UNR; ++u) {
+        const int jj = min(jb + u * TPB + wave * TPW + lane / LPT, cnt - 1);
+        rel[u] = LIST ? (int)list[jj] : jj;
+        const int t = t_begin + rel[u];
+        cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
+        prm[u] = kv.vp[(slot0 + t) * GPT + grp];
+      }
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int t = tb + u * TPB + wave * TPW + lane / LPT;
-      // clamped lanes repeat the last token: their weight is zero
-      const float p = t < t_end ? sc[t - t_begin] : 0.0f;
-      const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
-      const float s = (float)h_from_bits(prm[u] >> 16);
-      const float ps = p * s;
-      pm += p * m;
-      const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+      for (int u = 0; u < UNR; ++u) {
+        // clamped lanes repeat the last position: their weight is zero
+        const bool live = jb + u * TPB + wave * TPW + lane / LPT < cnt;
+        const float p = live ? sc[rel[u]] : 0.0f;
+        const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
+        const float s = (float)h_from_bits(prm[u] >> 16);
+        const float ps = p * s;
+        pm += p * m;
+        const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
-        acc[8 * k + 0] += ps * byte_f<0>(lo);
-        acc[8 * k + 1] += ps * byte_f<0>(hi);
-        acc[8 * k + 2] += ps * byte_f<1>(lo);
-        acc[8 * k + 3] += ps * byte_f<1>(hi);
-        acc[8 * k + 4] += ps * byte_f<2>(lo);
-        acc[8 * k + 5] += ps * byte_f<2>(hi);
-        acc[8 * k + 6] += ps * byte_f<3>(lo);
-        acc[8 * k + 7] += ps * byte_f<3>(hi);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
+          acc[8 * k + 0] += ps * byte_f<0>(lo);
+          acc[8 * k + 1] += ps * byte_f<0>(hi);
+          acc[8 * k + 2] += ps * byte_f<1>(lo);
+          acc[8 * k + 3] += ps * byte_f<1>(hi);
+          acc[8 * k + 4] += ps * byte_f<2>(lo);
+          acc[8 * k + 5] += ps * byte_f<2>(hi);
+          acc[8 * k + 6] += ps * byte_f<3>(lo);
+          acc[8 * k + 7] += ps * byte_f<3>(hi);
+        }
       }
     }
+  };
+  if constexpr (TOPK) {
+    if (use_list) v_pass(std::true_type{});
+    else v_pass(std::false_type{});
+  } else {
+    v_pass(std::false_type{});
   }
   // lanes of one wave that own the same dims: xor over the token bits of the lane id
 #pragma unroll
@@ -280,23 +428,31 @@ static DecPlan dec_plan(int B, int heads, int head_dim, int pos) {
   return p;
 }
 
-template <int HD, int UNR>
-static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
-                       const KVViewD& v, const int32_t* pad, f16* out, float* ws,
-                       float scale_log2, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<HD, UNR>), grid, dim3(256), 0, stream, qkv, b0, pos, v,
-                     pad, p.chunk, out, ws, scale_log2);
+// Dynamic LDS of a launch: the chunk's scores, plus the kept list for top-k.
+static size_t dec_lds_bytes(int chunk, bool topk) {
+  size_t b = (size_t)chunk * sizeof(float);
+  if (topk) b += (size_t)chunk * sizeof(uint16_t);
+  return (b + 15) / 16 * 16;
 }
 
-template <int HD>
+template <int HD, int UNR, bool TOPK>
 static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
                        const KVViewD& v, const int32_t* pad, f16* out, float* ws,
-                       float scale_log2, hipStream_t stream) {
+                       float scale_log2, float sparsity, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_decode_kernel<HD, UNR, TOPK>), grid, dim3(256),
+                     dec_lds_bytes(p.chunk, TOPK), stream, qkv, b0, pos, v, pad, p.chunk, out,
+                     ws, scale_log2, sparsity);
+}
+
+template <int HD, bool TOPK>
+static void launch_dec(const DecPlan& p, dim3 grid, const f16* qkv, int b0, int pos,
+                       const KVViewD& v, const int32_t* pad, f16* out, float* ws,
+                       float scale_log2, float sparsity, hipStream_t stream) {
   switch (p.unr) {
-    case 4: launch_dec<HD, 4>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
-    case 3: launch_dec<HD, 3>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
-    case 2: launch_dec<HD, 2>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
-    default: launch_dec<HD, 1>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, stream); break;
+    case 4: launch_dec<HD, 4, TOPK>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, sparsity, stream); break;
+    case 3: launch_dec<HD, 3, TOPK>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, sparsity, stream); break;
+    case 2: launch_dec<HD, 2, TOPK>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, sparsity, stream); break;
+    default: launch_dec<HD, 1, TOPK>(p, grid, qkv, b0, pos, v, pad, out, ws, scale_log2, sparsity, stream); break;
   }
 }
 
@@ -334,18 +490,50 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
   dim3 grid(p.splits, kv->heads, B);
   if (kv->head_dim == 64) {
-    launch_dec<64>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, (float*)ws,
-                   scale_log2, stream);
+    launch_dec<64, false>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, (float*)ws,
+                          scale_log2, 1.0f, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<64>, dim3(kv->heads, B), dim3(64), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);
   } else {
-    launch_dec<128>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, (float*)ws,
-                    scale_log2, stream);
+    launch_dec<128, false>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out,
+                           (float*)ws, scale_log2, 1.0f, stream);
     if (p.splits > 1)
       hipLaunchKernelGGL(attn_decode_merge_kernel<128>, dim3(kv->heads, B), dim3(128), 0, stream,
                          (const float*)ws, p.splits, kv->heads, (f16*)out);
   }
+  FLEXQ_LAUNCH_CHECK();
+  return FLEXQ_OK;
+}
+
+extern "C" int flexq_attn_decode_kv4_topk(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                                          const flexq_kv4_layer* kv, float sparsity,
+                                          uint16_t* out, hipStream_t stream) {
+  if (!(sparsity > 0.0f) || !(sparsity <= __FLT_MAX__)) return FLEXQ_ERR_INVALID;
+  if (!kv || !qkv || !out) return FLEXQ_ERR_INVALID;
+  if (B < 0 || b0 < 0 || pos < 0) return FLEXQ_ERR_INVALID;
+  if (B == 0) return FLEXQ_OK;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return FLEXQ_ERR_UNSUPPORTED;
+  if (kv->heads <= 0 || b0 + B > kv->batch || pos >= kv->max_len) return FLEXQ_ERR_INVALID;
+  if (!kv->k_codes || !kv->v_codes || !kv->k_params || !kv->v_params) return FLEXQ_ERR_INVALID;
+  if (((uintptr_t)qkv & 15) || ((uintptr_t)out & 1) || ((uintptr_t)kv->k_codes & 15) ||
+      ((uintptr_t)kv->v_codes & 15) || ((uintptr_t)kv->k_params & 3) || ((uintptr_t)kv->v_params & 3) ||
+      ((uintptr_t)kv->pad & 3))
+    return FLEXQ_ERR_INVALID;
+  if (kv->heads > 65535 || B > 65535) return FLEXQ_ERR_UNSUPPORTED;
+  if (pos + 1 > kDecMaxChunk) return FLEXQ_ERR_UNSUPPORTED;   // the scores live in LDS
+  const int step = kv->head_dim == 128 ? 64 : 128;
+  DecPlan p{1, pos + 1, dec_unroll((pos + 1 + step - 1) / step)};
+  KVViewD v{kv->k_codes, kv->v_codes, (uint32_t*)kv->k_params, (uint32_t*)kv->v_params, kv->heads,
+            kv->max_len};
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
+  dim3 grid(1, kv->heads, B);
+  if (kv->head_dim == 64)
+    launch_dec<64, true>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, nullptr,
+                         scale_log2, sparsity, stream);
+  else
+    launch_dec<128, true>(p, grid, (const f16*)qkv, b0, pos, v, kv->pad, (f16*)out, nullptr,
+                          scale_log2, sparsity, stream);
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
 }

@@ -102,7 +102,7 @@ struct TraceScope {
 int run_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t h, int32_t ffn,
               const uint16_t* x_in, int64_t rows, bool prefill, int32_t nb, int32_t S,
               int32_t b0, int32_t pos, uint16_t* x_out, const LayerScratch& s,
-              hipStream_t stream, flexq_trace* tr = nullptr) {
+              hipStream_t stream, flexq_trace* tr = nullptr, float sparsity = 0.0f) {
   TRY(flexq_layernorm(x_in, rows, h, h, L->ln1_g, L->ln1_b, s.a, stream));
   {
     TraceScope ts(tr, stream, FLEXQ_TRACE_QKV, rows);
@@ -110,6 +110,8 @@ int run_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t h, int32_
   }
   if (prefill)
     TRY(flexq_attn_prefill(s.qkv, nb, S, b0, kv, s.attn, stream));
+  else if (sparsity > 0.0f && sparsity < 1.0f)
+    TRY(flexq_attn_decode_kv4_topk(s.qkv, nb, b0, pos, kv, sparsity, s.attn, stream));
   else
     TRY(flexq_attn_decode_kv4(s.qkv, nb, b0, pos, kv, s.attn, s.ws, s.ws_bytes, stream));
   {
@@ -276,7 +278,7 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
     TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, B, false, B, 1, 0, pos, y, ls,
-                  stream, m->trace));
+                  stream, m->trace, m->attn_sparsity));
     std::swap(x, y);
   }
   return model_head(m, x, m->hidden, B, 0, pos, false, next, logits, s, stream);

@@ -21,6 +21,7 @@ EXPORTED = (
     "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
+    "flexq_attn_decode_kv4_topk",
     "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
 )
@@ -74,7 +75,8 @@ class ModelStruct(C.Structure):
                 ("embed", W4Struct), ("pos", C.c_void_p), ("lnf_g", C.c_void_p),
                 ("lnf_b", C.c_void_p), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct)),
-                ("gen", C.POINTER(GenConfig)), ("stopped", C.c_void_p)]
+                ("gen", C.POINTER(GenConfig)), ("stopped", C.c_void_p),
+                ("attn_sparsity", C.c_float)]
 
 
 _lib = None
@@ -105,6 +107,8 @@ def lib():
             "flexq_attn_decode_workspace_size": (sz, [i32, i32, i32, i32]),
             "flexq_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct), vp, vp,
                                                 sz, vp]),
+            "flexq_attn_decode_kv4_topk": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
+                                                     C.c_float, vp, vp]),
             "flexq_embed": (C.c_int, [vp, i64, i32, i32, vp, C.POINTER(W4Struct), vp, i32, vp,
                                       vp]),
             "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
@@ -393,6 +397,19 @@ def attn_decode(qkv, pos, kv: KV4, b0=0, out=None, ws=None, stream=None):
     return y
 
 
+def attn_decode_topk(qkv, pos, kv: KV4, sparsity, b0=0, out=None, stream=None):
+    """Sparse decode attention: each query keeps its ceil(sparsity * n) best positions."""
+    _need(qkv, torch.float16, "qkv")
+    B = qkv.shape[0]
+    h = kv.heads * kv.head_dim
+    y = out if out is not None else torch.empty(B, h, dtype=torch.float16, device=qkv.device)
+    kc = kv.c()
+    _check("flexq_attn_decode_kv4_topk", lib().flexq_attn_decode_kv4_topk(
+        qkv.data_ptr(), B, b0, pos, C.byref(kc), float(sparsity), y.data_ptr(),
+        _stream(stream)))
+    return y
+
+
 def embed(tokens, pos_base, seq, emb: W4, pos_table, out=None, stream=None, pad=None):
     _need(tokens, torch.int32, "tokens")
     n = tokens.numel()
@@ -525,6 +542,11 @@ class QModel:
                                    pos16.shape[0], self._layer_arr, self._kv_arr, embed_w4.c(),
                                    pos16.data_ptr(), lnf_g.data_ptr(), lnf_b.data_ptr(),
                                    self.workspace.data_ptr(), nbytes)
+
+    def set_attn_sparsity(self, sparsity=0.0):
+        """Decode attention keeps each query's ceil(sparsity * n) best positions when
+        0 < sparsity < 1; dense otherwise."""
+        self._struct.attn_sparsity = float(sparsity)
 
     def set_generation(self, gen=None):
         """Greedy (None) or a GenConfig for the following prefill / decode calls; with a

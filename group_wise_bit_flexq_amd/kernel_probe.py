@@ -6,6 +6,10 @@
     python -m group_wise_bit_flexq_amd.kernel_probe decode --workload opt175b --reps 2
         one decode step's 4-bit GEMMs (M = batch) and decode attention over a cache
         of prompt + gen/2 positions;
+    python -m group_wise_bit_flexq_amd.kernel_probe sparse --workload opt175b --reps 10
+        decode attention over a filled cache of prompt + gen/2 positions: dense, and
+        top-k sparse at sparsity 1, 0.5, 0.25, 0.1 (algorithmic bytes: every K, the
+        kept V);
     python -m group_wise_bit_flexq_amd.kernel_probe prefill_attn --workload opt175b --reps 3
         causal prefill attention of one micro-batch (micro_batch x prompt tokens, all
         heads) with the fused 4-bit KV store;
@@ -86,6 +90,36 @@ def decode(wl, reps):
     ms = _time(lambda: F.attn_decode(qkv, T, kv, out=out, ws=ws), reps)
     nbytes = wl.batch * wl.heads * (T + 1) * 2 * wl.head_dim * 0.5625
     res["attn_decode"] = {"T": T + 1, "ms": ms, "gbps": nbytes / ms / 1e6}
+    return res
+
+
+def sparse(wl, reps):
+    """Decode attention over a filled cache (random codes, offsets N(0, 0.25), steps
+    U(0.01, 0.1)): dense, then top-k at several sparsities."""
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    B, nh, hd = wl.batch, wl.heads, wl.head_dim
+    T = wl.prompt + wl.gen // 2
+    kv = F.KV4(B, nh, hd, T + 1)
+    for c in (kv.k_codes, kv.v_codes):
+        c.random_(0, 256)
+    for p in (kv.k_params, kv.v_params):
+        p[..., 0].normal_(0.0, 0.5)
+        p[..., 1].uniform_(0.01, 0.1)
+    qkv = torch.randn(B, 3 * wl.hidden, device="cuda").half()
+    out = torch.empty(B, wl.hidden, dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(F.attn_decode_ws_bytes(B, nh, hd, T), 16), dtype=torch.uint8,
+                     device="cuda")
+    row = hd * 0.5625                       # bytes of one position's K (or V) in one head
+    res = {"T": T + 1}
+    ms = _time(lambda: F.attn_decode(qkv, T, kv, out=out, ws=ws), reps)
+    res["dense"] = {"ms": ms, "gbps": B * nh * (T + 1) * 2 * row / ms / 1e6}
+    for sp in (1.0, 0.5, 0.25, 0.1):
+        k = max(1, int(-(-(sp * (T + 1)) // 1)))
+        ms = _time(lambda: F.attn_decode_topk(qkv, T, kv, sp, out=out), reps)
+        nbytes = B * nh * ((T + 1) + k) * row   # every K, the kept V
+        res[f"topk_{sp}"] = {"kept": k, "ms": ms, "gbps": nbytes / ms / 1e6}
     return res
 
 
@@ -176,8 +210,8 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "prefill_attn", "quant", "quant_ex", "stress",
-                                     "pick", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "sparse", "prefill_attn", "quant",
+                                     "quant_ex", "stress", "pick", "copy"])
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -190,6 +224,8 @@ def main():
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
+    elif a.what == "sparse":
+        r = sparse(wl, a.reps)
     elif a.what == "prefill_attn":
         r = prefill_attn(wl, a.reps)
     elif a.what == "quant":

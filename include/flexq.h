@@ -179,6 +179,9 @@ typedef struct {
    * flexq_prefill from the first token and kept by flexq_decode_step (needs a stop
    * token in gen). */
   int32_t* stopped;
+  /* decode attention: dense unless 0 < attn_sparsity < 1, then top-k sparse (see
+   * flexq_attn_decode_kv4_topk) */
+  float attn_sparsity;
 } flexq_model;
 
 const char* flexq_status_string(int status);
@@ -278,6 +281,18 @@ size_t flexq_attn_decode_workspace_size(int32_t B, int32_t heads, int32_t head_d
 int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
                           const flexq_kv4_layer* kv, uint16_t* out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* Sparse decode attention (source notes "Flex Opt": the `attn_sparsity` policy, whose
+ * mechanism the pages leave open).  As flexq_attn_decode_kv4, except that each query
+ * keeps only the k = max(1, ceil(min(sparsity, 1) * n)) highest of its n scores
+ * (n = pos + 1 - pad, the product in fp32; among equal scores the lower position
+ * first) and takes the softmax over those alone.  One work-group per (sequence,
+ * head), no workspace; needs pos + 1 <= 4096 (FLEXQ_ERR_UNSUPPORTED beyond) and
+ * 0 < sparsity <= FLT_MAX (FLEXQ_ERR_INVALID otherwise).  Kept scores are decided
+ * in fp32, as computed by the kernel. */
+int flexq_attn_decode_kv4_topk(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                               const flexq_kv4_layer* kv, float sparsity, uint16_t* out,
+                               hipStream_t stream);
 
 /* ---------------------------------------------------------------- model pieces
  * Token + position embedding (`opt_input_embed`, source notes "Pytorch Backend"):

@@ -380,10 +380,10 @@ def attn_prefill(qkv, batch, seq, heads, head_dim, cache: KVCache | None = None,
 
 
 def topk_count(sparsity, n):
-    """Positions kept by sparse attention over n candidates: k = ceil(sparsity * n), the
-    product taken in float32 (sparsity a float32), at least 1 and at most n."""
-    k = int(np.ceil(np.float32(sparsity) * np.float32(n)))
-    return min(max(k, 1), n)
+    """Positions kept by sparse attention over n candidates: k = ceil(min(sparsity, 1) * n),
+    the product taken in float32 (sparsity a float32), at least 1."""
+    k = int(np.ceil(min(np.float32(sparsity), np.float32(1)) * np.float32(n)))
+    return max(k, 1)
 
 
 def attn_decode(qkv, pos, cache: KVCache, b0=0, sparsity=1.0):
