@@ -1,8 +1,8 @@
 """Build libflexq.so (the HIP kernels and the C ABI of include/flexq.h) for gfx950.
 
-Every csrc/*.hip file is compiled to an object with hipcc, in parallel, and the
-objects are linked into group_wise_bit_flexq_amd/libflexq.so.  Objects go to
-_build/ at the repository root.
+Every csrc/*.hip file is compiled to an object with hipcc and every csrc/*.cpp file
+(host-only code) with ROCm's clang++, in parallel, and the objects are linked into
+group_wise_bit_flexq_amd/libflexq.so.  Objects go to _build/ at the repository root.
 """
 from __future__ import annotations
 
@@ -18,6 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflexq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CLANGXX = os.environ.get("FLEXQ_CXX", "/opt/rocm/llvm/bin/clang++")
 ARCH = "gfx950"
 
 CFLAGS = [
@@ -28,16 +29,29 @@ CFLAGS = [
 ]
 
 
+# host-only code: x86-64-v3 (AVX2, FMA, F16C) and no floating-point contraction, so the
+# quantizer's code decisions see the same fp32 operations as the GPU's
+HOST_CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-march=x86-64-v3", "-ffp-contract=off",
+    "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{INCLUDE}",
+]
+
+
 def _sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    base, ext = os.path.splitext(os.path.basename(src))
+    obj = os.path.join(BUILD, base + (".o" if ext == ".hip" else ".host.o"))
+    if ext == ".hip":
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [CLANGXX, *HOST_CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"compile failed for {src}:\n{r.stderr}")
     return obj
 
 

@@ -21,7 +21,7 @@ EXPORTED = (
     "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
-    "flexq_attn_decode_kv4_topk",
+    "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4",
     "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
 )
@@ -109,6 +109,8 @@ def lib():
                                                 sz, vp]),
             "flexq_attn_decode_kv4_topk": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
                                                      C.c_float, vp, vp]),
+            "flexq_host_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
+                                                     vp, i32]),
             "flexq_embed": (C.c_int, [vp, i64, i32, i32, vp, C.POINTER(W4Struct), vp, i32, vp,
                                       vp]),
             "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
@@ -217,19 +219,24 @@ class KV4:
     """The 4-bit KV cache of one layer (see flexq_kv4_layer); `pad` is None or a device
     int32 [batch] tensor of left-padding counts."""
 
-    def __init__(self, batch, heads, head_dim, max_len, device="cuda", pad=None):
+    def __init__(self, batch, heads, head_dim, max_len, device="cuda", pad=None, pin=False):
+        """device "cuda" for the GPU kernels; "cpu" for a host-memory cache (pinned with
+        pin=True, for asynchronous copies) served by flexq_host_attn_decode_kv4."""
         self.batch, self.heads, self.head_dim, self.max_len = batch, heads, head_dim, max_len
+        dev = torch.device(device)
         if pad is not None:
-            _need(pad, torch.int32, "pad")
+            if pad.dtype != torch.int32 or not pad.is_contiguous() or pad.device.type != dev.type:
+                raise ValueError(f"pad: expected a contiguous int32 tensor on {dev.type}")
             if pad.numel() != batch:
                 raise ValueError("pad: one entry per cache row")
         self.pad = pad
         shp = (batch, heads, max_len, head_dim // 2)
         pshp = (batch, heads, max_len, head_dim // 64, 2)
-        self.k_codes = torch.zeros(shp, dtype=torch.uint8, device=device)
-        self.v_codes = torch.zeros(shp, dtype=torch.uint8, device=device)
-        self.k_params = torch.zeros(pshp, dtype=torch.float16, device=device)
-        self.v_params = torch.zeros(pshp, dtype=torch.float16, device=device)
+        kw = dict(device=dev, pin_memory=True) if (pin and dev.type == "cpu") else dict(device=dev)
+        self.k_codes = torch.zeros(shp, dtype=torch.uint8, **kw)
+        self.v_codes = torch.zeros(shp, dtype=torch.uint8, **kw)
+        self.k_params = torch.zeros(pshp, dtype=torch.float16, **kw)
+        self.v_params = torch.zeros(pshp, dtype=torch.float16, **kw)
 
     def c(self) -> KV4Struct:
         return KV4Struct(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
@@ -394,6 +401,21 @@ def attn_decode(qkv, pos, kv: KV4, b0=0, out=None, ws=None, stream=None):
     _check("flexq_attn_decode_kv4", lib().flexq_attn_decode_kv4(
         qkv.data_ptr(), B, b0, pos, C.byref(kc), y.data_ptr(), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return y
+
+
+def host_attn_decode(qkv, pos, kv: KV4, b0=0, out=None, threads=0):
+    """Decode attention on the host CPU over a host-memory cache (CPU tensors)."""
+    if qkv.device.type != "cpu" or qkv.dtype != torch.float16 or not qkv.is_contiguous():
+        raise ValueError("qkv: expected a contiguous float16 CPU tensor")
+    if kv.k_codes.device.type != "cpu":
+        raise ValueError("kv: expected a host-memory cache")
+    B = qkv.shape[0]
+    h = kv.heads * kv.head_dim
+    y = out if out is not None else torch.empty(B, h, dtype=torch.float16)
+    kc = kv.c()
+    _check("flexq_host_attn_decode_kv4", lib().flexq_host_attn_decode_kv4(
+        qkv.data_ptr(), B, b0, pos, C.byref(kc), y.data_ptr(), int(threads)))
     return y
 
 

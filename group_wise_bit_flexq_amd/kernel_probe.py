@@ -10,6 +10,9 @@
         decode attention over a filled cache of prompt + gen/2 positions: dense, and
         top-k sparse at sparsity 1, 0.5, 0.25, 0.1 (algorithmic bytes: every K, the
         kept V);
+    python -m group_wise_bit_flexq_amd.kernel_probe host_attn --workload opt175b --reps 5 --threads 16
+        decode attention on the host CPU over a host-memory cache for one micro-batch of
+        sequences (prompt + gen/2 positions), beside the host's multi-threaded read rate;
     python -m group_wise_bit_flexq_amd.kernel_probe prefill_attn --workload opt175b --reps 3
         causal prefill attention of one micro-batch (micro_batch x prompt tokens, all
         heads) with the fused 4-bit KV store;
@@ -123,6 +126,42 @@ def sparse(wl, reps):
     return res
 
 
+def host_attn(wl, reps, threads):
+    """Decode attention on the host CPU over a host-memory cache: the sequences of one
+    micro-batch of the workload (prompt + gen/2 positions, random codes), beside the
+    host's multi-threaded read rate (a float32 sum over 2 GiB)."""
+    import time
+
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    B, nh, hd = wl.micro_batch, wl.heads, wl.head_dim
+    T = wl.prompt + wl.gen // 2
+    kv = F.KV4(B, nh, hd, T + 1, device="cpu")
+    for c in (kv.k_codes, kv.v_codes):
+        c.random_(0, 256)
+    for p in (kv.k_params, kv.v_params):
+        p[..., 0].normal_(0.0, 0.5)
+        p[..., 1].uniform_(0.01, 0.1)
+    qkv = torch.randn(B, 3 * wl.hidden).half()
+    out = torch.empty(B, wl.hidden, dtype=torch.float16)
+    F.host_attn_decode(qkv, T, kv, out=out, threads=threads)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        F.host_attn_decode(qkv, T, kv, out=out, threads=threads)
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    nbytes = B * nh * (T + 1) * 2 * hd * 0.5625
+    torch.set_num_threads(threads)
+    x = torch.rand(1 << 29)
+    x.sum()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        x.sum()
+    read_gbps = x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    return {"B": B, "heads": nh, "T": T + 1, "threads": threads, "ms": ms,
+            "gbps": nbytes / ms / 1e6, "host_read_gbps": read_gbps}
+
+
 def prefill_attn(wl, reps):
     import torch
 
@@ -210,8 +249,9 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "sparse", "prefill_attn", "quant",
-                                     "quant_ex", "stress", "pick", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "sparse", "host_attn", "prefill_attn",
+                                     "quant", "quant_ex", "stress", "pick", "copy"])
+    ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
@@ -224,6 +264,8 @@ def main():
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
+    elif a.what == "host_attn":
+        r = host_attn(wl, a.reps, a.threads)
     elif a.what == "sparse":
         r = sparse(wl, a.reps)
     elif a.what == "prefill_attn":

@@ -294,6 +294,20 @@ int flexq_attn_decode_kv4_topk(const uint16_t* qkv, int32_t B, int32_t b0, int32
                                const flexq_kv4_layer* kv, float sparsity, uint16_t* out,
                                hipStream_t stream);
 
+/* Decode attention on the host CPU over a 4-bit cache in HOST memory (source notes
+ * "Flex Opt": the cpu_cache_compute policy and the load_cache path that attends in
+ * a CPU workspace; "Pytorch Backend": mha_gen over a compressed cache dequantized
+ * to fp32).  For caches too large for HBM: only the new token's q, k, v and the
+ * output cross the host link.  Same arithmetic contract as flexq_attn_decode_kv4
+ * (quantize-append at pos with the same code decisions, bit for bit; positions
+ * [pad, pos]; fp32 scores and softmax; fp16 output).  Every pointer is a HOST
+ * pointer: qkv fp16 [B][3h], out fp16 [B][h], and all arrays of kv (pad included).
+ * Runs synchronously on `threads` host threads (<= 0: one per hardware thread),
+ * one (sequence, head) pair per thread at a time, so results do not depend on the
+ * thread count; returns when done.  No stream, no GPU. */
+int flexq_host_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                               const flexq_kv4_layer* kv, uint16_t* out, int32_t threads);
+
 /* ---------------------------------------------------------------- model pieces
  * Token + position embedding (`opt_input_embed`, source notes "Pytorch Backend"):
  * out[m] = fp16(dequant(embed row tokens[m]) + pos[p + 2]) with position
