@@ -2,8 +2,9 @@
 // Opt": an OPT model is an embedding, N transformer layers and an output head;
 // per layer the engine runs compute_layer between cache loads/stores).
 //
-// Every tensor is resident in HBM, so a layer is a fixed chain of kernel launches
-// on the caller's stream with no host synchronisation:
+// With every tensor resident in HBM a layer is a fixed chain of kernel launches on
+// the caller's stream with no host synchronisation (a host-DRAM cache tier adds one
+// wait per decode layer, for the CPU's share of the attention):
 //   LN1 -> QKV linear (+bias) -> attention (prefill: causal MFMA + KV4 store,
 //   decode: KV4 append + split-K) -> out linear (+bias, +residual) -> LN2 ->
 //   FC1 (+bias, ReLU) -> FC2 (+bias, +residual).
@@ -99,21 +100,47 @@ struct TraceScope {
   }
 };
 
+// Decode rows >= row0 whose cache is in host memory: their attention runs on the CPU.
+struct HostSplit {
+  const flexq_kv4_layer* kv;  // this layer's host cache
+  int32_t row0, threads;
+  uint16_t *qkv, *out;        // pinned host staging
+};
+
 int run_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t h, int32_t ffn,
               const uint16_t* x_in, int64_t rows, bool prefill, int32_t nb, int32_t S,
               int32_t b0, int32_t pos, uint16_t* x_out, const LayerScratch& s,
-              hipStream_t stream, flexq_trace* tr = nullptr, float sparsity = 0.0f) {
+              hipStream_t stream, flexq_trace* tr = nullptr, float sparsity = 0.0f,
+              const HostSplit* hs = nullptr) {
   TRY(flexq_layernorm(x_in, rows, h, h, L->ln1_g, L->ln1_b, s.a, stream));
   {
     TraceScope ts(tr, stream, FLEXQ_TRACE_QKV, rows);
     TRY(flexq_linear_w4(s.a, rows, &L->wqkv, L->bqkv, nullptr, 0, s.qkv, s.ws, s.ws_bytes, stream));
   }
-  if (prefill)
+  if (prefill) {
     TRY(flexq_attn_prefill(s.qkv, nb, S, b0, kv, s.attn, stream));
-  else if (sparsity > 0.0f && sparsity < 1.0f)
-    TRY(flexq_attn_decode_kv4_topk(s.qkv, nb, b0, pos, kv, sparsity, s.attn, stream));
-  else
-    TRY(flexq_attn_decode_kv4(s.qkv, nb, b0, pos, kv, s.attn, s.ws, s.ws_bytes, stream));
+  } else {
+    const int32_t nd = hs ? std::min(nb, hs->row0) : nb;  // rows with a device cache
+    const int32_t nhost = nb - nd;
+    if (nhost > 0) {  // the host rows' q, k, v must be in host memory before the CPU starts
+      if (hipMemcpyAsync(hs->qkv, s.qkv + (size_t)nd * 3 * h, (size_t)nhost * 3 * h * 2,
+                         hipMemcpyDeviceToHost, stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess)
+        return FLEXQ_ERR_DEVICE;
+    }
+    if (nd > 0) {  // enqueued first, so the GPU attends while the CPU does
+      if (sparsity > 0.0f && sparsity < 1.0f)
+        TRY(flexq_attn_decode_kv4_topk(s.qkv, nd, b0, pos, kv, sparsity, s.attn, stream));
+      else
+        TRY(flexq_attn_decode_kv4(s.qkv, nd, b0, pos, kv, s.attn, s.ws, s.ws_bytes, stream));
+    }
+    if (nhost > 0) {
+      TRY(flexq_host_attn_decode_kv4(hs->qkv, nhost, 0, pos, hs->kv, hs->out, hs->threads));
+      if (hipMemcpyAsync(s.attn + (size_t)nd * h, hs->out, (size_t)nhost * h * 2,
+                         hipMemcpyHostToDevice, stream) != hipSuccess)
+        return FLEXQ_ERR_DEVICE;
+    }
+  }
   {
     TraceScope ts(tr, stream, FLEXQ_TRACE_OUT, rows);
     TRY(flexq_linear_w4(s.attn, rows, &L->wo, L->bo, x_in, 0, s.x1, s.ws, s.ws_bytes, stream));
@@ -161,10 +188,62 @@ int check_model(const flexq_model* m) {
     return FLEXQ_ERR_INVALID;
   if (m->embed.rows != m->vocab || m->embed.cols != m->hidden || !m->workspace)
     return FLEXQ_ERR_INVALID;
+  if (const flexq_host_tier* t = m->host) {
+    if (!t->kv || t->row0 < 0 || t->row0 > m->kv[0].batch) return FLEXQ_ERR_INVALID;
+    if (m->attn_sparsity > 0.0f && m->attn_sparsity < 1.0f) return FLEXQ_ERR_UNSUPPORTED;
+    for (int l = 0; l < m->layers; ++l)
+      if (t->kv[l].heads != m->heads || t->kv[l].head_dim != m->hidden / m->heads ||
+          t->kv[l].batch != t->kv[0].batch || t->kv[l].max_len != t->kv[0].max_len)
+        return FLEXQ_ERR_INVALID;
+  }
+  return FLEXQ_OK;
+}
+
+// The device staging copy of one host micro-batch's K/V: nb rows laid out as a cache.
+flexq_kv4_layer stage_view(const flexq_model* m, int32_t nb, int32_t b0) {
+  const flexq_host_tier* t = m->host;
+  const int32_t hd = m->hidden / m->heads;
+  const size_t codes = (size_t)nb * m->heads * t->kv[0].max_len * (hd / 2);
+  const size_t params = (size_t)nb * m->heads * t->kv[0].max_len * (hd / 64) * 2;  // fp16s
+  char* p = (char*)t->stage;
+  flexq_kv4_layer v;
+  v.k_codes = (uint8_t*)p;
+  v.v_codes = (uint8_t*)(p + codes);
+  v.k_params = (uint16_t*)(p + 2 * codes);
+  v.v_params = (uint16_t*)(p + 2 * codes + params * 2);
+  v.batch = nb;
+  v.heads = m->heads;
+  v.head_dim = hd;
+  v.max_len = t->kv[0].max_len;
+  v.pad = m->kv[0].pad ? m->kv[0].pad + b0 : nullptr;
+  return v;
+}
+
+// Copies the staged rows into host cache rows [r0, r0 + nb) of one layer.
+int stage_to_host(const flexq_kv4_layer& st, const flexq_kv4_layer& hk, int32_t r0,
+                  hipStream_t stream) {
+  const size_t per_row_codes = (size_t)st.heads * st.max_len * (st.head_dim / 2);
+  const size_t per_row_params = (size_t)st.heads * st.max_len * (st.head_dim / 64) * 2;
+  const size_t nc = per_row_codes * st.batch, np = per_row_params * st.batch;
+  if (hipMemcpyAsync(hk.k_codes + per_row_codes * r0, st.k_codes, nc, hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipMemcpyAsync(hk.v_codes + per_row_codes * r0, st.v_codes, nc, hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipMemcpyAsync(hk.k_params + per_row_params * r0, st.k_params, np * 2,
+                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipMemcpyAsync(hk.v_params + per_row_params * r0, st.v_params, np * 2,
+                     hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return FLEXQ_ERR_DEVICE;
   return FLEXQ_OK;
 }
 
 }  // namespace
+
+extern "C" size_t flexq_host_stage_size(int32_t heads, int32_t head_dim, int32_t nb,
+                                        int32_t max_len) {
+  if (heads <= 0 || nb <= 0 || max_len <= 0 || (head_dim != 64 && head_dim != 128)) return 0;
+  return (size_t)nb * heads * max_len * (head_dim / 2 + (head_dim / 64) * 4) * 2;
+}
 
 extern "C" size_t flexq_layer_workspace_size(int32_t hidden, int32_t heads, int32_t ffn,
                                              int64_t rows, int32_t max_len) {
@@ -240,7 +319,17 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
   if (nb < 0 || S < 0 || b0 < 0 || !tokens || !next) return FLEXQ_ERR_INVALID;
   if (nb == 0 || S == 0) return FLEXQ_OK;
   // cache rows (pad counts and stopped flags are indexed by them before any layer runs)
-  if ((int64_t)b0 + nb > m->kv[0].batch || S > m->kv[0].max_len) return FLEXQ_ERR_INVALID;
+  const flexq_host_tier* ht = m->host;
+  const bool host_rows = ht && b0 >= ht->row0;
+  if (host_rows) {
+    if ((int64_t)b0 - ht->row0 + nb > ht->kv[0].batch || S > ht->kv[0].max_len)
+      return FLEXQ_ERR_INVALID;
+    if (!ht->stage || ht->stage_bytes < flexq_host_stage_size(m->heads, m->hidden / m->heads, nb,
+                                                              ht->kv[0].max_len))
+      return FLEXQ_ERR_INVALID;
+  } else if ((int64_t)b0 + nb > m->kv[0].batch || S > m->kv[0].max_len) {
+    return FLEXQ_ERR_INVALID;   // also a micro-batch that straddles the host tier
+  }
   const int64_t rows = (int64_t)nb * S;
   ModelScratch s;
   TRY(model_scratch(m, rows, nb, 0, &s));
@@ -251,10 +340,17 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
   layer_carve(s.layer_base, m->hidden, m->heads, m->ffn, rows, 0, &ls);
   uint16_t* x = s.x0;
   uint16_t* y = s.x1;
+  const flexq_kv4_layer stage = host_rows ? stage_view(m, nb, b0) : flexq_kv4_layer{};
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
-    TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, rows, true, nb, S, b0, 0, y, ls,
-                  stream, m->trace));
+    if (host_rows) {  // K/V through the device stage, then to the host tier
+      TRY(run_layer(&m->layer[l], &stage, m->hidden, m->ffn, x, rows, true, nb, S, 0, 0, y, ls,
+                    stream, m->trace));
+      TRY(stage_to_host(stage, ht->kv[l], b0 - ht->row0, stream));
+    } else {
+      TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, rows, true, nb, S, b0, 0, y,
+                    ls, stream, m->trace));
+    }
     std::swap(x, y);
   }
   return model_head(m, x + (int64_t)(S - 1) * m->hidden, (int64_t)S * m->hidden, nb, b0, S - 1,
@@ -266,7 +362,14 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
   TRY(check_model(m));
   if (B < 0 || pos < 0 || !tokens || !next) return FLEXQ_ERR_INVALID;
   if (B == 0) return FLEXQ_OK;
-  if (B > m->kv[0].batch || pos >= m->kv[0].max_len) return FLEXQ_ERR_INVALID;
+  const flexq_host_tier* ht = m->host;
+  const int32_t nhost = ht ? std::max(0, B - ht->row0) : 0;
+  if (B - nhost > m->kv[0].batch || pos >= m->kv[0].max_len) return FLEXQ_ERR_INVALID;
+  if (nhost > 0) {
+    if (nhost > ht->kv[0].batch || pos >= ht->kv[0].max_len) return FLEXQ_ERR_INVALID;
+    if (!ht->host_ws || ht->host_ws_bytes < (size_t)nhost * 4 * m->hidden * 2)
+      return FLEXQ_ERR_INVALID;
+  }
   ModelScratch s;
   TRY(model_scratch(m, B, B, pos + 1, &s));
   TRY(flexq_embed(tokens, B, pos, 1, m->kv[0].pad, &m->embed, m->pos, m->pos_rows, s.x0,
@@ -277,8 +380,12 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
   uint16_t* y = s.x1;
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
+    HostSplit hs{};
+    if (nhost > 0)
+      hs = HostSplit{&ht->kv[l], ht->row0, ht->threads, (uint16_t*)ht->host_ws,
+                     (uint16_t*)ht->host_ws + (size_t)nhost * 3 * m->hidden};
     TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, B, false, B, 1, 0, pos, y, ls,
-                  stream, m->trace, m->attn_sparsity));
+                  stream, m->trace, m->attn_sparsity, nhost > 0 ? &hs : nullptr));
     std::swap(x, y);
   }
   return model_head(m, x, m->hidden, B, 0, pos, false, next, logits, s, stream);

@@ -21,7 +21,7 @@ EXPORTED = (
     "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
-    "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4",
+    "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4", "flexq_host_stage_size",
     "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
 )
@@ -68,6 +68,13 @@ class GenConfig(C.Structure):
                 ("stop", C.c_int32)]
 
 
+class HostTierStruct(C.Structure):
+    """flexq_host_tier: cache rows >= row0 in host memory, attended on the CPU."""
+    _fields_ = [("kv", C.POINTER(KV4Struct)), ("row0", C.c_int32), ("threads", C.c_int32),
+                ("host_ws", C.c_void_p), ("host_ws_bytes", C.c_size_t),
+                ("stage", C.c_void_p), ("stage_bytes", C.c_size_t)]
+
+
 class ModelStruct(C.Structure):
     _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("pos_rows", C.c_int32),
@@ -76,7 +83,7 @@ class ModelStruct(C.Structure):
                 ("lnf_b", C.c_void_p), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct)),
                 ("gen", C.POINTER(GenConfig)), ("stopped", C.c_void_p),
-                ("attn_sparsity", C.c_float)]
+                ("attn_sparsity", C.c_float), ("host", C.POINTER(HostTierStruct))]
 
 
 _lib = None
@@ -111,6 +118,7 @@ def lib():
                                                      C.c_float, vp, vp]),
             "flexq_host_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
                                                      vp, i32]),
+            "flexq_host_stage_size": (sz, [i32, i32, i32, i32]),
             "flexq_embed": (C.c_int, [vp, i64, i32, i32, vp, C.POINTER(W4Struct), vp, i32, vp,
                                       vp]),
             "flexq_argmax": (C.c_int, [vp, i64, i64, vp, vp]),
@@ -227,8 +235,8 @@ class KV4:
         if pad is not None:
             if pad.dtype != torch.int32 or not pad.is_contiguous() or pad.device.type != dev.type:
                 raise ValueError(f"pad: expected a contiguous int32 tensor on {dev.type}")
-            if pad.numel() != batch:
-                raise ValueError("pad: one entry per cache row")
+            if pad.numel() < batch:
+                raise ValueError("pad: at least one entry per cache row")
         self.pad = pad
         shp = (batch, heads, max_len, head_dim // 2)
         pshp = (batch, heads, max_len, head_dim // 64, 2)
@@ -538,10 +546,16 @@ def decode_layer(layer: QLayer, kv: KV4, x, pos, b0=0, out=None, ws=None, stream
 
 
 class QModel:
-    """An OPT-shaped model with 4-bit weights and per-layer 4-bit KV caches."""
+    """An OPT-shaped model with 4-bit weights and per-layer 4-bit KV caches.
+
+    host_rows > 0 keeps the caches of the last host_rows sequences in pinned host
+    memory (flexq_host_tier): their decode attention runs on host_threads CPU threads;
+    their prefill micro-batches (at most max_prefill_batch sequences) go through a
+    device staging area."""
 
     def __init__(self, layers: list, embed_w4: W4, pos16, lnf_g, lnf_b, heads, batch, max_len,
-                 max_prefill_rows, device="cuda"):
+                 max_prefill_rows, device="cuda", host_rows=0, host_threads=0,
+                 max_prefill_batch=None):
         self.layers = layers
         self.embed = embed_w4
         self.pos = pos16
@@ -552,9 +566,13 @@ class QModel:
         self.ffn = layers[0].ffn
         self.batch, self.max_len = batch, max_len
         hd = self.hidden // heads
-        # left padding of each cache row, shared by every layer's cache (0: none)
+        if not 0 <= host_rows <= batch:
+            raise ValueError("host_rows outside [0, batch]")
+        self.row0 = batch - host_rows
+        # left padding of each cache row, shared by every layer's cache (0: none); the
+        # device array covers every row (the embedding reads it), the host one the host rows
         self.pad = torch.zeros(batch, dtype=torch.int32, device=device)
-        self.caches = [KV4(batch, heads, hd, max_len, device, pad=self.pad) for _ in layers]
+        self.caches = [KV4(self.row0, heads, hd, max_len, device, pad=self.pad) for _ in layers]
         nbytes = lib().flexq_model_workspace_size(self.hidden, heads, self.ffn, self.vocab,
                                                   max_prefill_rows, batch, max_len)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -564,6 +582,21 @@ class QModel:
                                    pos16.shape[0], self._layer_arr, self._kv_arr, embed_w4.c(),
                                    pos16.data_ptr(), lnf_g.data_ptr(), lnf_b.data_ptr(),
                                    self.workspace.data_ptr(), nbytes)
+        self.host_caches = []
+        if host_rows > 0:
+            self.host_pad = torch.zeros(host_rows, dtype=torch.int32, pin_memory=True)
+            self.host_caches = [KV4(host_rows, heads, hd, max_len, "cpu", pad=self.host_pad,
+                                    pin=True) for _ in layers]
+            self._host_kv_arr = (KV4Struct * len(layers))(*[k.c() for k in self.host_caches])
+            self.host_ws = torch.empty(host_rows * 4 * self.hidden, dtype=torch.float16,
+                                       pin_memory=True)
+            nb = max_prefill_batch or host_rows
+            sb = lib().flexq_host_stage_size(heads, hd, nb, max_len)
+            self.stage = torch.empty(max(sb, 16), dtype=torch.uint8, device=device)
+            self._host = HostTierStruct(self._host_kv_arr, self.row0, int(host_threads),
+                                        self.host_ws.data_ptr(), self.host_ws.numel() * 2,
+                                        self.stage.data_ptr(), sb)
+            self._struct.host = C.pointer(self._host)
 
     def set_attn_sparsity(self, sparsity=0.0):
         """Decode attention keeps each query's ceil(sparsity * n) best positions when
@@ -587,10 +620,11 @@ class QModel:
         nb, S = tokens.shape
         if b0 < 0 or b0 + nb > self.batch:
             raise ValueError("prefill rows outside the cache")
-        if pad is None:
-            self.pad[b0:b0 + nb].zero_()
-        else:
-            self.pad[b0:b0 + nb].copy_(torch.as_tensor(pad, dtype=torch.int32).reshape(nb))
+        p = torch.zeros(nb, dtype=torch.int32) if pad is None else \
+            torch.as_tensor(pad, dtype=torch.int32).reshape(nb).cpu()
+        self.pad[b0:b0 + nb].copy_(p)
+        if self.host_caches and b0 >= self.row0:
+            self.host_pad[b0 - self.row0:b0 - self.row0 + nb].copy_(p)
         nxt = next_out if next_out is not None else torch.empty(nb, dtype=torch.int32,
                                                                 device=tokens.device)
         _need(nxt, torch.int32, "next_out")

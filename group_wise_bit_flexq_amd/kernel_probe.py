@@ -13,6 +13,9 @@
     python -m group_wise_bit_flexq_amd.kernel_probe host_attn --workload opt175b --reps 5 --threads 16
         decode attention on the host CPU over a host-memory cache for one micro-batch of
         sequences (prompt + gen/2 positions), beside the host's multi-threaded read rate;
+    python -m group_wise_bit_flexq_amd.kernel_probe host_tier --workload opt30b --reps 3 --threads 16
+        the whole OPT-30B-shaped model with its last micro-batch's caches in host memory,
+        beside the all-device model: prefill per micro-batch and decode step times;
     python -m group_wise_bit_flexq_amd.kernel_probe prefill_attn --workload opt175b --reps 3
         causal prefill attention of one micro-batch (micro_batch x prompt tokens, all
         heads) with the fused 4-bit KV store;
@@ -162,6 +165,52 @@ def host_attn(wl, reps, threads):
             "gbps": nbytes / ms / 1e6, "host_read_gbps": read_gbps}
 
 
+def host_tier(wl, reps, threads):
+    """Whole-model timing with the last micro-batch's caches in host memory
+    (flexq_host_tier) beside the all-device model on the same weights: prefill time of
+    a device and of a host micro-batch, and the decode step time."""
+    import time
+
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    from group_wise_bit_flexq_amd.workloads import POS_ROWS
+    h, f, nh, mb, S = wl.hidden, wl.ffn, wl.heads, wl.micro_batch, wl.prompt
+    layers = []
+    for l in range(wl.layers):
+        w16 = synth.layer_weights_fp16(h, f, 0, l, device="cuda")
+        layers.append(F.QLayer.from_fp16(w16, nh, "cuda"))
+        del w16
+    emb = F.quantize_weight(synth.model_tensor("embed", (wl.vocab, h), 0, "cuda"))
+    pos = synth.model_tensor("pos", (POS_ROWS, h), 0, "cuda")
+    g = synth.model_tensor("lnf_g", (h,), 0, "cuda")
+    b = synth.model_tensor("lnf_b", (h,), 0, "cuda")
+    toks = synth.token_ids(wl.batch, S, wl.vocab, 1).cuda()
+    res = {"host_rows": mb, "threads": threads}
+    for name, hr in (("device", 0), ("host_tier", mb)):
+        m = F.QModel(layers, emb, pos, g, b, nh, wl.batch, wl.max_len, mb * S, "cuda",
+                     host_rows=hr, host_threads=threads, max_prefill_batch=mb)
+        pre = []
+        for j in range(wl.batch // mb):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m.prefill(toks[j * mb:(j + 1) * mb], b0=j * mb)
+            torch.cuda.synchronize()
+            pre.append((time.perf_counter() - t0) * 1e3)
+        cur = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+        m.decode_step(cur, S)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            m.decode_step(cur, S + 1 + i)
+        torch.cuda.synchronize()
+        res[name] = {"prefill_ms": pre, "decode_step_ms": (time.perf_counter() - t0) * 1e3 / reps}
+        del m
+        torch.cuda.empty_cache()
+    return res
+
+
 def prefill_attn(wl, reps):
     import torch
 
@@ -249,8 +298,9 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "sparse", "host_attn", "prefill_attn",
-                                     "quant", "quant_ex", "stress", "pick", "copy"])
+    ap.add_argument("what", choices=["gemm", "decode", "sparse", "host_attn", "host_tier",
+                                     "prefill_attn", "quant", "quant_ex", "stress", "pick",
+                                     "copy"])
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
@@ -264,6 +314,8 @@ def main():
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
+    elif a.what == "host_tier":
+        r = host_tier(wl, a.reps, a.threads)
     elif a.what == "host_attn":
         r = host_attn(wl, a.reps, a.threads)
     elif a.what == "sparse":

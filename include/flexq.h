@@ -155,6 +155,34 @@ typedef struct {
   int32_t stop;
 } flexq_gen_config;
 
+/* Host-DRAM tier of the KV cache (source notes "Flex Opt": cache placement between
+ * GPU and CPU, the cpu_cache_compute policy, and the load_cache path that splits a
+ * batch's attention between the GPU and the CPU).  Model cache rows >= row0 live in
+ * HOST memory (host row r - row0), for batches whose 4-bit cache does not fit in
+ * HBM; rows < row0 stay in the device caches `kv`.  A decode step copies the host
+ * rows' q, k, v to host_ws, runs their attention on the CPU (threads, as
+ * flexq_host_attn_decode_kv4) while the GPU attends the device rows, and copies
+ * the outputs back: the call blocks the host once per layer and cannot be captured
+ * in a graph.  A prefill micro-batch must lie wholly on one side of row0; a host
+ * micro-batch writes its K/V to the device `stage` area, then copies them to the
+ * host caches.  With left padding, kv[0].pad must hold all model rows (the
+ * embedding reads it) and each kv[l] of the host tier its own host rows' pads.
+ *   kv        HOST array of `layers` caches in pinned HOST memory (batch = host rows)
+ *   host_ws   pinned HOST memory, >= (decode batch - row0) * 4 * hidden * 2 bytes
+ *   stage     DEVICE memory, >= flexq_host_stage_size(heads, head_dim, nb, max_len)
+ *             for the largest host prefill micro-batch nb (max_len of the host tier) */
+typedef struct {
+  const flexq_kv4_layer* kv;
+  int32_t row0;
+  int32_t threads; /* CPU threads for the host rows' attention (<= 0: all) */
+  void* host_ws;
+  size_t host_ws_bytes;
+  void* stage;
+  size_t stage_bytes;
+} flexq_host_tier;
+
+size_t flexq_host_stage_size(int32_t heads, int32_t head_dim, int32_t nb, int32_t max_len);
+
 /* A whole OPT-shaped model.  Non-owning: every pointer stays the caller's.
  * `layer` and `kv` are HOST arrays of `layers` entries (the structs inside hold
  * device pointers).  embed is the 4-bit token embedding [vocab][hidden], also used
@@ -182,6 +210,9 @@ typedef struct {
   /* decode attention: dense unless 0 < attn_sparsity < 1, then top-k sparse (see
    * flexq_attn_decode_kv4_topk) */
   float attn_sparsity;
+  /* NULL, or a HOST host-tier description (see flexq_host_tier); not combined with
+   * sparse attention */
+  const flexq_host_tier* host;
 } flexq_model;
 
 const char* flexq_status_string(int status);
