@@ -115,14 +115,6 @@ __device__ __forceinline__ f16x2 dequant_pair(f16x2 c, f16x2 s2, f16x2 m2) {
 
 }  // namespace flexq
 
-namespace flexq {
-// Token choice shared by flexq_argmax, flexq_pick and the model's output head;
-// `fresh` ignores the incoming stopped flags (the first token of a sequence).
-int launch_pick(const float* logits, int64_t M, int64_t N, const flexq_gen_config* gen,
-                int32_t step, int32_t m0, int32_t* stopped, bool fresh, int32_t* next,
-                hipStream_t stream);
-}  // namespace flexq
-
 #define FLEXQ_LAUNCH_CHECK()                               \
   do {                                                     \
     if (hipGetLastError() != hipSuccess) return FLEXQ_ERR_DEVICE; \

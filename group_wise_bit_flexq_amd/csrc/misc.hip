@@ -3,6 +3,7 @@
 // source notes, section "Pytorch Backend".  All HBM-bound and small next to the
 // GEMMs and attention.
 #include "common.h"
+#include "pick.h"
 
 namespace flexq {
 

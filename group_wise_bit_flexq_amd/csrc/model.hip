@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "pick.h"
 
 namespace {
 
