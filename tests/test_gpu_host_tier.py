@@ -4,7 +4,8 @@ GPU attends the rest.  The prefill of host rows (through the device stage) leave
 same codes and params as an all-device run, bit for bit; greedy generation, ragged
 prompts included, follows the oracle teacher-forced (logits within 2e-2 max-abs /
 1e-2 relative Frobenius, tokens identical except where the oracle's own top-2 gap is
-within twice the logit error); unsupported combinations are rejected."""
+within twice the logit error); unsupported combinations are rejected; and sampling with
+a stop token over a ragged batch half in the host tier picks what the oracle picks."""
 import numpy as np
 import pytest
 import torch
@@ -110,3 +111,41 @@ def test_host_tier_rejects():
     gm.set_attn_sparsity(0.5)
     with pytest.raises(F.FlexqError):
         gm.decode_step(torch.zeros(B, dtype=torch.int32, device="cuda"), S)
+
+
+def test_host_tier_sampling_stop_and_padding_together():
+    # every generation feature at once: temperature sampling with a stop token over a
+    # ragged batch whose last micro-batch lives in the host tier; each step's tokens are
+    # the oracle's pick on the GPU's own logits, and the logits follow the oracle model
+    F = require_gpu()
+    from tests.test_gpu_model import _host_model
+    nh, B, S, G, mb, host_rows = 4, 6, 40, 6, 3, 3
+    _say("host tier + sampling + stop + padding")
+    parts = _host_model(256, nh, 1024, 1000, 2, 13)
+    V = parts[1].shape[0]
+    toks = synth.token_ids(B, S, V, synth.sub_seed(0, "tokens")).cuda()
+    pad = np.array([3, 0, 30, 7, 0, 25], np.int32)
+    gm = _model(F, parts, nh, B, S + G - 1, mb, S, host_rows)
+    free = _model(F, parts, nh, B, S + G - 1, mb, S, host_rows)
+    cfg = dict(do_sample=True, temperature=0.9, seed=77, stop=-1)
+    free.set_generation(F.gen_config(**cfg))
+    _, fo = _generate(free, toks, S, G, mb, V, pad)
+    stop = int(fo[4, 1])                      # a host-tier row's second token
+    cfg["stop"] = stop
+    gm.set_generation(F.gen_config(**cfg))
+    gl, go = _generate(gm, toks, S, G, mb, V, pad)
+    from tests.test_gpu_sampling import _assert_same_picks
+    stopped = np.zeros(B, bool)
+    for i in range(G):
+        want = O.pick(gl[i], cfg, S - 1 + i, 0, stopped)
+        _assert_same_picks(go[:, i], want, gl[i], cfg, S - 1 + i, 0)
+        stopped |= go[:, i] == stop
+    assert np.all(go[4, 1:] == stop)
+    from tests.test_gpu_model import _oracle_model
+    om = _oracle_model(parts, nh)
+    caches = om.new_caches(B, S + G - 1)
+    lg, _ = om.prefill(to_np(toks), caches, pad=pad)
+    for i in range(G):
+        if i > 0:
+            lg, _ = om.decode_step(go[:, i - 1], S + i - 1, caches)
+        assert_north_star(gl[i], lg, f"combined logits step {i}")
