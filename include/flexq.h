@@ -394,9 +394,13 @@ int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32
                   int32_t* next, float* logits, hipStream_t stream);
 
 /* One decode step of B sequences (cache rows 0..B-1): tokens int32 [B]
- * at position pos -> next [B] (and logits [B][vocab] if not NULL).  The call
- * neither synchronises nor allocates, so a caller may capture it in a HIP graph
- * (pos is baked into the captured kernels). */
+ * at position pos -> next [B] (and logits [B][vocab] if not NULL).  Without a
+ * host tier the call neither synchronises nor allocates, so a caller may capture
+ * it in a HIP graph (pos and the generation config are baked into the captured
+ * kernels); with host rows it waits on the stream once per layer (see
+ * flexq_host_tier).  Errors: B beyond the caches, pos >= max_len, a too small
+ * host staging area -> FLEXQ_ERR_INVALID; sparse attention with a host tier ->
+ * FLEXQ_ERR_UNSUPPORTED. */
 int flexq_decode_step(const flexq_model* m, const int32_t* tokens, int32_t B, int32_t pos,
                       int32_t* next, float* logits, hipStream_t stream);
 
