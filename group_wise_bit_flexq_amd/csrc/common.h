@@ -97,10 +97,33 @@ __device__ __forceinline__ void codes_to_bytes(uint32_t w, uint32_t& t0, uint32_
   t1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
+// The 4-bit weight layout keeps the eight codes of each 32-bit word in the order a
+// spread to bytes needs no permute: byte j holds code j (low nibble) and code j + 4
+// (high nibble).  w4_word_from_codes converts a word from the packed order above.
+__device__ __forceinline__ uint32_t w4_word_from_codes(uint32_t w) {
+  uint32_t t0, t1;
+  codes_to_bytes(w, t0, t1);
+  return t0 | (t1 << 4);
+}
+__device__ __forceinline__ void w4_word_to_bytes(uint32_t w, uint32_t& t0, uint32_t& t1) {
+  t0 = w & 0x0F0F0F0Fu;
+  t1 = (w >> 4) & 0x0F0F0F0Fu;
+}
+
 // The four exact code pairs (c_2j, c_2j+1), j = 0..3, of one packed word.
 __device__ __forceinline__ void codes_to_pairs(uint32_t w, f16x2 out[4]) {
   uint32_t t0, t1;
   codes_to_bytes(w, t0, t1);
+  out[0] = code_pair_f16<false>(t0);
+  out[1] = code_pair_f16<true>(t0);
+  out[2] = code_pair_f16<false>(t1);
+  out[3] = code_pair_f16<true>(t1);
+}
+
+// The same for a word of the weight layout.
+__device__ __forceinline__ void w4_word_to_pairs(uint32_t w, f16x2 out[4]) {
+  uint32_t t0, t1;
+  w4_word_to_bytes(w, t0, t1);
   out[0] = code_pair_f16<false>(t0);
   out[1] = code_pair_f16<true>(t0);
   out[2] = code_pair_f16<false>(t1);

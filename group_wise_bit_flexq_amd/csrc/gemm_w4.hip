@@ -240,7 +240,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_w4_big_kernel(
     dq_s = h2_from_u32((rp_##SET >> 16) * 0x10001u);      \
     dq_m = h2_from_u32((rp_##SET & 0xFFFFu) * 0x10001u);  \
   } while (0)
-#define DQ_PRE(W) codes_to_bytes((W), dq_t0, dq_t1)
+#define DQ_PRE(W) w4_word_to_bytes((W), dq_t0, dq_t1)
 // pair p of the word: elements 2p and 2p + 1
 #define DQ_PAIR(p) \
   dq##p = u32_from_h2(dequant_pair(code_pair_f16<(p) & 1>((p) < 2 ? dq_t0 : dq_t1), dq_s, dq_m))
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_skinny_kernel(
     dq_s1 = h2_from_u32((rp1_##SET >> 16) * 0x10001u);        \
     dq_m1 = h2_from_u32((rp1_##SET & 0xFFFFu) * 0x10001u);    \
   } while (0)
-#define DQ_PRE(W) codes_to_bytes((W), dq_t0, dq_t1)
+#define DQ_PRE(W) w4_word_to_bytes((W), dq_t0, dq_t1)
 // elements 2p, 2p + 1 of B fragment F[j]
 #define DQ_PAIR(F, j, p)                                                                   \
   do {                                                                                     \
@@ -735,7 +735,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
   do {                                                                              \
     s2 = h2_from_u32(((PW) >> 16) * 0x10001u);                                      \
     m2 = h2_from_u32(((PW) & 0xFFFFu) * 0x10001u);                                  \
-    codes_to_bytes(CW, t0, t1);                                                     \
+    w4_word_to_bytes(CW, t0, t1);                                                   \
     const f16x2 _d0 = dequant_pair(code_pair_f16<false>(t0), s2, m2);               \
     const f16x2 _d1 = dequant_pair(code_pair_f16<true>(t0), s2, m2);                \
     const f16x2 _d2 = dequant_pair(code_pair_f16<false>(t1), s2, m2);               \

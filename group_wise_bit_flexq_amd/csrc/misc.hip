@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     const f16x2 m2 = h2_from_u32((prm & 0xFFFFu) * 0x10001u);
     const f16x2 s2 = h2_from_u32((prm >> 16) * 0x10001u);
     f16x2 pr[8];
-    codes_to_pairs(cw.x, pr);
-    codes_to_pairs(cw.y, pr + 4);
+    w4_word_to_pairs(cw.x, pr);
+    w4_word_to_pairs(cw.y, pr + 4);
     const f16x8* pp = (const f16x8*)(pos + (int64_t)p * h + c * 16);
     const f16x8 p0 = pp[0], p1 = pp[1];
     f16x8 o0, o1;

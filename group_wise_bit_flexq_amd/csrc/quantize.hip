@@ -15,8 +15,9 @@ constexpr int kQThreads = 256;
 constexpr int kQGroupsPerBlock = kQThreads / kQLanes;
 
 // WEIGHT = false: codes and params in row-major group order.  WEIGHT = true: the 4-bit
-// weight layout (blocks of 128 rows, k-tile major, see w4_code_off); ngroups then counts
-// the rows padded to a multiple of 128, and the groups of pad rows are stored as zeros.
+// weight layout (blocks of 128 rows, k-tile major, see w4_code_off; codes of a word in
+// the order of w4_word_from_codes); ngroups then counts the rows padded to a multiple
+// of 128, and the groups of pad rows are stored as zeros.
 template <bool WEIGHT>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x,
                                                              uint2* __restrict__ codes,
@@ -44,7 +45,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     if constexpr (WEIGHT) {
       if (g >= nreal) packed[0] = packed[1] = p = 0;
       const int64_t row = g / KT, kt = g - row * KT;
-      codes[w4_code_off(row, kt, KT) / 8 + part] = make_uint2(packed[0], packed[1]);
+      codes[w4_code_off(row, kt, KT) / 8 + part] =
+          make_uint2(w4_word_from_codes(packed[0]), w4_word_from_codes(packed[1]));
       if (part == 0) params[w4_param_idx(row, kt, KT)] = p;
     } else {
       codes[g * 4 + part] = make_uint2(packed[0], packed[1]);

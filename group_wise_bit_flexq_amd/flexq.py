@@ -181,8 +181,9 @@ W4_BLOCK_ROWS = 128
 
 class W4:
     """A 4-bit weight [rows][cols] in the weight layout of flexq_w4: rows in blocks of
-    128, k-tile major.  codes uint8 [rows_pad/128][cols/64][128][32], params fp16
-    [rows_pad/128][cols/64][128][2] (rows_pad = rows rounded up to 128, pad rows zero)."""
+    128, k-tile major, codes of each 4-byte word with its first four in the low nibbles.
+    codes uint8 [rows_pad/128][cols/64][128][32], params fp16 [rows_pad/128][cols/64][128][2]
+    (rows_pad = rows rounded up to 128, pad rows zero)."""
 
     def __init__(self, codes: torch.Tensor, params: torch.Tensor, rows: int):
         if codes.dim() != 4 or codes.shape[2:] != (W4_BLOCK_ROWS, 32):
@@ -210,12 +211,20 @@ class W4:
         pad = nb * W4_BLOCK_ROWS - rows
         c = torch.nn.functional.pad(codes, (0, 0, 0, pad)).view(nb, W4_BLOCK_ROWS, kt, 32)
         p = torch.nn.functional.pad(params, (0, 0, 0, 0, 0, pad)).view(nb, W4_BLOCK_ROWS, kt, 2)
+        # within each 4-byte word: codes 0..7 of the word, then low nibbles = codes 0..3
+        w = c.reshape(nb, W4_BLOCK_ROWS, kt, 8, 4)
+        e = torch.stack((w & 15, w >> 4), dim=-1).reshape(nb, W4_BLOCK_ROWS, kt, 8, 8)
+        c = (e[..., :4] | (e[..., 4:] << 4)).reshape(nb, W4_BLOCK_ROWS, kt, 32)
         return W4(c.permute(0, 2, 1, 3).contiguous(), p.permute(0, 2, 1, 3).contiguous(), rows)
 
     def rowmajor(self):
         """(codes [rows][cols/2], params [rows][cols/64][2]) in row-major group order."""
         nb, kt = self.codes.shape[0], self.codes.shape[1]
-        c = self.codes.permute(0, 2, 1, 3).reshape(nb * W4_BLOCK_ROWS, kt * 32)[:self.rows]
+        w = self.codes.reshape(nb, kt, W4_BLOCK_ROWS, 8, 4)
+        e = torch.cat((w & 15, w >> 4), dim=-1)              # codes 0..7 of each word
+        w = e[..., 0::2] | (e[..., 1::2] << 4)              # back to the packed order
+        c = w.reshape(nb, kt, W4_BLOCK_ROWS, 32).permute(0, 2, 1, 3)
+        c = c.reshape(nb * W4_BLOCK_ROWS, kt * 32)[:self.rows]
         p = self.params.permute(0, 2, 1, 3).reshape(nb * W4_BLOCK_ROWS, kt, 2)[:self.rows]
         return c, p
 

@@ -59,15 +59,18 @@ typedef struct {
  * along cols (one group = 64 columns = one k-tile), in the weight layout written by
  * flexq_quantize_w4: rows in blocks of FLEXQ_W4_BLOCK_ROWS = 128, and within block b
  * the k-tiles in order, each holding the block's 128 rows contiguously:
- *   codes  byte  ((r / 128) * (cols/64) + kt) * 4096 + (r % 128) * 32 + j
- *          holds elements 64 kt + 2 j (low nibble) and 64 kt + 2 j + 1 (high nibble)
- *          of row r (j = 0..31);
+ *   codes  byte  ((r / 128) * (cols/64) + kt) * 4096 + (r % 128) * 32 + 4 q + j
+ *          holds elements 64 kt + 8 q + j (low nibble) and 64 kt + 8 q + j + 4 (high
+ *          nibble) of row r (q = 0..7, j = 0..3: within each 32-bit word the
+ *          low nibbles hold its first four codes, so spreading a word to one code per
+ *          byte takes one AND and one shift);
  *   params word  ((r / 128) * (cols/64) + kt) * 128 + (r % 128) = (offset, scale)
  *          as two fp16 (offset in the low half) of group kt of row r.
  * Both arrays cover rows padded up to a multiple of 128 (FLEXQ_W4_CODES_BYTES /
  * FLEXQ_W4_PARAMS_BYTES); pad rows hold zeros.  Codes and params are those of
  * flexq_quantize, only their order differs: a k-tile of any run of rows is read in
- * whole cache lines, which streaming the weights at small batch needs. */
+ * whole cache lines, which streaming the weights at small batch needs, and a code
+ * word expands to fp16 with two fewer instructions. */
 #define FLEXQ_W4_BLOCK_ROWS 128
 #define FLEXQ_W4_CODES_BYTES(rows, cols) \
   ((((rows) + 127) / 128) * 128 * (int64_t)(cols) / 2)

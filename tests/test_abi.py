@@ -55,7 +55,13 @@ def test_weight_layout_reordering_matches_header_formulas(rows, cols):
     for r in range(rows):
         for kt in range(KT):
             b = ((r // 128) * KT + kt) * 4096 + (r % 128) * 32
-            assert np.array_equal(flat_c[b:b + 32], codes[r, 32 * kt:32 * kt + 32])
+            # element e of the k-tile: packed order, byte e // 2, nibble e % 2
+            row = codes[r, 32 * kt:32 * kt + 32]
+            el = np.stack((row & 15, row >> 4), axis=1).reshape(64)
+            for q in range(8):
+                for j in range(4):
+                    got = flat_c[b + 4 * q + j]
+                    assert got & 15 == el[8 * q + j] and got >> 4 == el[8 * q + j + 4], (r, kt, q, j)
             assert flat_p[((r // 128) * KT + kt) * 128 + r % 128] == params[r, kt].view(np.uint32)[0]
     pad_rows = [r for r in range(rows, nb * 128)]
     for r in pad_rows[:5]:

@@ -68,8 +68,10 @@ def test_quantize_weight_layout_bit_exact(rows, cols):
     r = np.arange(rows)[:, None]
     kt = np.arange(KT)[None, :]
     base = ((r // 128) * KT + kt) * 4096 + (r % 128) * 32
-    got_c = flat_c[base[:, :, None] + np.arange(32)[None, None, :]].reshape(rows, cols // 2)
-    assert np.array_equal(got_c, codes)
+    got_c = flat_c[base[:, :, None] + np.arange(32)[None, None, :]].reshape(rows, KT, 8, 4)
+    # byte 4 q + j of a k-tile holds elements 8 q + j (low nibble) and 8 q + j + 4 (high)
+    el = np.concatenate((got_c & 15, got_c >> 4), axis=-1).reshape(rows, cols)
+    assert np.array_equal(el, O.unpack_nibbles(codes))
     got_p = flat_p[((r // 128) * KT + kt) * 128 + (r % 128)]
     assert np.array_equal(got_p, params.view(np.uint32).reshape(rows, KT))
     nb = (rows + 127) // 128
