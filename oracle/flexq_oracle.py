@@ -22,7 +22,7 @@ its codes are integers decided by floating point, so it takes those decisions in
 fp32, the precision of the kernel it checks (IEEE division, round-to-nearest-even,
 no fused multiply-add), as a fixed sequence written out in `quantize`.
 
-Readings of the pages where they leave a step open (each also listed in the design doc):
+Readings of the pages where they leave a step open:
   * per group: offset = group minimum, scale = step = (max - min) / 15, both fp16;
     [WALK] section 6.3 names one fp16 "scale" tensor; an asymmetric (symmetric=False)
     code needs an offset as well, so the params hold the pair (offset, scale);

@@ -35,7 +35,7 @@ def assert_close_fp16(got, ref, extra=0.0, what=""):
                              f"got {g[tuple(i)]} ref {r[tuple(i)]} bound {np.broadcast_to(bound, r.shape)[tuple(i)]}")
 
 
-def assert_north_star(got, ref, what="", atol=2e-2, rel_frob=1e-2):
+def assert_logits_close(got, ref, what="", atol=2e-2, rel_frob=1e-2):
     """Layer outputs / logits: max-abs <= 2e-2 and relative Frobenius <= 1e-2."""
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)

@@ -15,7 +15,7 @@ import torch
 from group_wise_bit_flexq_amd import synth
 from group_wise_bit_flexq_amd.workloads import POS_ROWS, WORKLOADS
 from oracle import flexq_oracle as O
-from tests.gpu_helpers import F16, assert_close_fp16, assert_north_star, require_gpu, to_np
+from tests.gpu_helpers import F16, assert_close_fp16, assert_logits_close, require_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -100,13 +100,13 @@ def test_layer_opt125m_free_running():
     oc = O.KVCache(B, nh, hd, S + G)
     x = synth.normal_fp16((B * S, h), 1.0, synth.sub_seed(0, "x", 0))
     y = F.prefill_layer(L, kv, x.cuda(), B, S)
-    assert_north_star(to_np(y), ol.prefill(x.numpy(), B, S, oc), "prefill layer")
+    assert_logits_close(to_np(y), ol.prefill(x.numpy(), B, S, oc), "prefill layer")
     flips = (to_np(kv.k_codes) != oc.k_codes).mean() + (to_np(kv.v_codes) != oc.v_codes).mean()
     assert flips < 1e-3, f"KV code flips {flips}"
     for i in range(G):
         xd = synth.normal_fp16((B, h), 1.0, synth.sub_seed(0, "xd", i))
         yd = F.decode_layer(L, kv, xd.cuda(), S + i)
-        assert_north_star(to_np(yd), ol.decode(xd.numpy(), S + i, oc), f"decode step {i}")
+        assert_logits_close(to_np(yd), ol.decode(xd.numpy(), S + i, oc), f"decode step {i}")
 
 
 def _host_model(h, nh, f, V, L, seed):
@@ -161,7 +161,7 @@ def _greedy_check(F, parts, nh, B, S, G, mb, sample):
         if i > 0:
             lg, nx = om.decode_step(go[:, i - 1], S + i - 1, caches)
             print(f"oracle decode step {i}", flush=True)
-        err, rf = assert_north_star(gl[i], lg, f"logits step {i}")
+        err, rf = assert_logits_close(gl[i], lg, f"logits step {i}")
         worst.append(err)
         for r in range(len(sample)):
             if nx[r] != go[r, i]:
