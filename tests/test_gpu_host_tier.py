@@ -149,3 +149,18 @@ def test_host_tier_sampling_stop_and_padding_together():
         if i > 0:
             lg, _ = om.decode_step(go[:, i - 1], S + i - 1, caches)
         assert_logits_close(gl[i], lg, f"combined logits step {i}")
+
+
+def test_all_rows_in_the_host_tier():
+    # no device cache rows at all: every prefill goes through the stage, every decode
+    # attention runs on the CPU
+    F = require_gpu()
+    from tests.test_gpu_model import _host_model
+    nh, B, S, G, mb = 4, 2, 24, 4, 2
+    _say("all rows in the host tier")
+    parts = _host_model(256, nh, 1024, 1000, 1, 14)
+    V = parts[1].shape[0]
+    toks = synth.token_ids(B, S, V, synth.sub_seed(0, "tokens")).cuda()
+    gm = _model(F, parts, nh, B, S + G - 1, mb, S, B)
+    gl, go = _generate(gm, toks, S, G, mb, V)
+    assert _follow_oracle(parts, nh, toks, gl, go, S, G) <= 1

@@ -244,3 +244,17 @@ def test_tiny_model_sparse_decode():
         for r in range(B):
             if nx[r] != go[r, i]:
                 assert lg[r].max() - lg[r, go[r, i]] <= 2 * err + 1e-6, (i, r)
+
+
+def test_attn_decode_topk_single_position():
+    # pos 0: one candidate, kept whatever the sparsity; the output is that position's value
+    F = require_gpu()
+    _say("attn_decode_topk at pos 0")
+    rng = np.random.default_rng(92)
+    nh, hd = 2, 64
+    kv = F.KV4(1, nh, hd, 4)
+    oc = O.KVCache(1, nh, hd, 4)
+    q1 = _qkv(rng, 1, nh, hd)
+    got = to_np(F.attn_decode_topk(torch.from_numpy(q1).cuda(), 0, kv, 0.01))
+    ref = O.attn_decode(q1, 0, oc, sparsity=0.01)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
