@@ -580,10 +580,11 @@ class QModel:
             x = L.decode(x, pos, c, b0, sparsity)
         return lm_head(x, self.lnf_g, self.lnf_b, self.e_codes, self.e_params, self.e_w)
 
-    def generate(self, tokens, gen, config=None, pad=None):
+    def generate(self, tokens, gen, config=None, pad=None, sparsity=1.0):
         """Generation of `gen` tokens ([WALK] section 4.1): greedy without `config`, else
         `pick` with it (do_sample, temperature, seed, stop); `pad` = left padding of each
-        prompt (the attention mask of a ragged batch)."""
+        prompt (the attention mask of a ragged batch); `sparsity` < 1: top-k decode
+        attention (see attn_decode)."""
         tokens = np.asarray(tokens)
         nb, seq = tokens.shape
         caches = self.new_caches(nb, seq + gen - 1)
@@ -593,7 +594,7 @@ class QModel:
             nxt = pick(lg, config, seq - 1, 0, stopped)
         out = [nxt]
         for i in range(gen - 1):
-            lg, nxt = self.decode_step(nxt, seq + i, caches)
+            lg, nxt = self.decode_step(nxt, seq + i, caches, sparsity=sparsity)
             if config is not None:
                 nxt = pick(lg, config, seq + i, 0, stopped)
             out.append(nxt)

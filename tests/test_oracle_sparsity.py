@@ -98,3 +98,13 @@ def test_dense_limit_and_padding(rng):
     got = O.attn_decode(qkv, S, c1, sparsity=1 / 3)
     ref = O.attn_decode(qkv, S - 12, c3, sparsity=1 / 3)
     assert np.array_equal(got, ref)
+
+
+def test_generate_with_full_sparsity_is_dense(rng):
+    from tests.test_oracle_model import _tiny_model
+    m = _tiny_model(rng, L=1, h=128, nh=2, f=256, V=100)
+    tok = rng.integers(0, 100, size=(2, 6))
+    assert np.array_equal(m.generate(tok, 4, sparsity=1.0), m.generate(tok, 4))
+    # one kept position per query: still a valid generation of the right shape
+    out = m.generate(tok, 4, sparsity=1e-6)
+    assert out.shape == (2, 4) and out.min() >= 0 and out.max() < 100
