@@ -155,9 +155,19 @@ __device__ void topk_compact(const float* sc, int n, uint16_t* list) {
   __syncthreads();
 }
 
-// byte N of a word as float (one v_cvt_f32_ubyteN)
-template <int N>
-__device__ __forceinline__ float byte_f(uint32_t w) { return (float)((w >> (8 * N)) & 0xFFu); }
+// Sum of x over the lanes of a 16-lane row whose index agrees with this lane's modulo
+// STEP (DPP row rotations; every such lane ends with the same sum).
+template <int STEP>
+__device__ __forceinline__ float row_sum_stride(float x) {
+  if constexpr (STEP < 16) {
+    constexpr int kRowRor = 0x120 + STEP;  // DPP row_ror:STEP
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, x), kRowRor, 0xF, 0xF, false));
+    return row_sum_stride<STEP * 2>(x);
+  } else {
+    return x;
+  }
+}
 
 template <int HD, int UNR, bool TOPK>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict__ qkv, int b0,
@@ -172,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   constexpr int GPT = HD / 64;     // quantization groups per token vector
   // dynamic LDS: the split's scores (chunk floats), then for top-k the kept list
   extern __shared__ __attribute__((aligned(16))) float sc[];
-  __shared__ float red[4][HD + LPT];
+  __shared__ float red[16][HD + LPT];   // per 16-lane row: V sums and offset terms
   __shared__ float wred[8];
 
   const int split = blockIdx.x, head = blockIdx.y, bi = blockIdx.z;
@@ -331,15 +341,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
         const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+          // two exact fp16 codes per convert; each feeds an fp32 FMA (v_fma_mix_f32)
           const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
-          acc[8 * k + 0] += ps * byte_f<0>(lo);
-          acc[8 * k + 1] += ps * byte_f<0>(hi);
-          acc[8 * k + 2] += ps * byte_f<1>(lo);
-          acc[8 * k + 3] += ps * byte_f<1>(hi);
-          acc[8 * k + 4] += ps * byte_f<2>(lo);
-          acc[8 * k + 5] += ps * byte_f<2>(hi);
-          acc[8 * k + 6] += ps * byte_f<3>(lo);
-          acc[8 * k + 7] += ps * byte_f<3>(hi);
+          const f16x2 e02 = code_pair_f16<false>(lo), e46 = code_pair_f16<true>(lo);
+          const f16x2 e13 = code_pair_f16<false>(hi), e57 = code_pair_f16<true>(hi);
+          acc[8 * k + 0] = __builtin_fmaf(ps, (float)e02.x, acc[8 * k + 0]);
+          acc[8 * k + 1] = __builtin_fmaf(ps, (float)e13.x, acc[8 * k + 1]);
+          acc[8 * k + 2] = __builtin_fmaf(ps, (float)e02.y, acc[8 * k + 2]);
+          acc[8 * k + 3] = __builtin_fmaf(ps, (float)e13.y, acc[8 * k + 3]);
+          acc[8 * k + 4] = __builtin_fmaf(ps, (float)e46.x, acc[8 * k + 4]);
+          acc[8 * k + 5] = __builtin_fmaf(ps, (float)e57.x, acc[8 * k + 5]);
+          acc[8 * k + 6] = __builtin_fmaf(ps, (float)e46.y, acc[8 * k + 6]);
+          acc[8 * k + 7] = __builtin_fmaf(ps, (float)e57.y, acc[8 * k + 7]);
         }
       }
     }
@@ -350,25 +363,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   } else {
     v_pass(std::false_type{});
   }
-  // lanes of one wave that own the same dims: xor over the token bits of the lane id
+  // lanes of one 16-lane row that own the same dims (lane = LPT * token + j) are summed
+  // with DPP rotations; each row's sums go to LDS for the output step
 #pragma unroll
-  for (int o = LPT; o < 64; o <<= 1) {
+  for (int e = 0; e < 32; ++e) acc[e] = row_sum_stride<LPT>(acc[e]);
+  pm = row_sum_stride<LPT>(pm);
+  const int rw = wave * 4 + (lane >> 4);
+  if ((lane & 15) < LPT) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
-    pm += __shfl_xor(pm, o, 64);
-  }
-  if (lane < LPT) {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) red[wave][32 * lane + e] = acc[e];
-    red[wave][HD + lane] = pm;
+    for (int e = 0; e < 32; ++e) red[rw][32 * j + e] = acc[e];
+    red[rw][HD + j] = pm;
   }
   __syncthreads();
 
-  // ---- 5. output (one thread per dim)
+  // ---- 5. output (one thread per dim): the 16 row sums in a fixed order
   if (tid < HD) {
     const int d = tid, pj = d / 32;
-    const float od = ((red[0][d] + red[1][d]) + (red[2][d] + red[3][d])) +
-                     ((red[0][HD + pj] + red[1][HD + pj]) + (red[2][HD + pj] + red[3][HD + pj]));
+    float od = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) od += red[r][d] + red[r][HD + pj];
     if (nsplit == 1) {
       out[(int64_t)bi * h + head * HD + d] = (f16)(od / lsum);
     } else {
