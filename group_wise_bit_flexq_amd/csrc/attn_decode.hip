@@ -155,6 +155,20 @@ __device__ void topk_compact(const float* sc, int n, uint16_t* list) {
   __syncthreads();
 }
 
+// Sum of x over the N (1, 2 or 4) consecutive lanes of an aligned group (DPP quad
+// permutations: lane ^ 1, then lane ^ 2).
+template <int N>
+__device__ __forceinline__ float quad_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4, "lanes per token");
+  if constexpr (N >= 2)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  return x;
+}
+
 // Sum of x over the lanes of a 16-lane row whose index agrees with this lane's modulo
 // STEP (DPP row rotations; every such lane ends with the same sum).
 template <int STEP>
@@ -187,7 +201,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
 
   const int split = blockIdx.x, head = blockIdx.y, bi = blockIdx.z;
   const int nsplit = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nh = kv.nh;
   const int h = nh * HD;
   const int T = pos + 1;
@@ -224,19 +239,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   // ---- this lane's slice of q: dims 32 j .. 32 j + 31 (group j / 2)
   const int j = lane % LPT;
   const int grp = j >> 1;
-  f16x2 q2[16];
+  // q pairs in the order the K pass forms code pairs: for the 8 dims of word k,
+  // qe[2k] = (q0, q2), qe[2k+1] = (q4, q6), qo[2k] = (q1, q3), qo[2k+1] = (q5, q7)
+  f16x2 qe[8], qo[8];
   float qsum = 0.0f;
   {
     const uint4* qp = (const uint4*)(row + head * HD + 32 * j);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 u = qp[c];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        q2[c * 4 + k] = h2_from_u32(w[k]);
-        qsum += (float)q2[c * 4 + k].x + (float)q2[c * 4 + k].y;
-      }
+      const f16x2 a = h2_from_u32(u.x), b = h2_from_u32(u.y), cc = h2_from_u32(u.z),
+                  d = h2_from_u32(u.w);
+      qe[2 * c] = f16x2{a.x, b.x};
+      qe[2 * c + 1] = f16x2{cc.x, d.x};
+      qo[2 * c] = f16x2{a.y, b.y};
+      qo[2 * c + 1] = f16x2{cc.y, d.y};
+      qsum += (((float)a.x + (float)a.y) + ((float)b.x + (float)b.y)) +
+              (((float)cc.x + (float)cc.y) + ((float)d.x + (float)d.y));
     }
   }
 
@@ -256,21 +275,23 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     for (int u = 0; u < UNR; ++u) {
       const int t = tb + u * TPB + wave * TPW + lane / LPT;
       const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
-      float dot = 0.0f;
+      // code pairs as fp16 subnormals: even dims c * 2^-24 from the low nibbles, odd
+      // dims 16 c * 2^-24 from the high nibbles left in place (exact products; the
+      // odd-dim sum is scaled by 1/16 once per token)
+      float dlo = 0.0f, dhi = 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
-        // code pairs as fp16 subnormals c * 2^-24, element order (2i, 2i+1)
-        dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c040c00u)), q2[4 * k + 0], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c050c01u)), q2[4 * k + 1], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c060c02u)), q2[4 * k + 2], dot, false);
-        dot = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, lo, 0x0c070c03u)), q2[4 * k + 3], dot, false);
+        const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = w[k] & 0xF0F0F0F0u;
+        dlo = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(lo, lo, 0x0c010c00u)), qe[2 * k], dlo, false);
+        dlo = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(lo, lo, 0x0c030c02u)), qe[2 * k + 1], dlo, false);
+        dhi = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, hi, 0x0c010c00u)), qo[2 * k], dhi, false);
+        dhi = __builtin_amdgcn_fdot2(h2_from_u32(__builtin_amdgcn_perm(hi, hi, 0x0c030c02u)), qo[2 * k + 1], dhi, false);
       }
+      const float dot = __builtin_fmaf(dhi, 0.0625f, dlo);
       const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
       const float s = (float)h_from_bits(prm[u] >> 16);
       float partial = (s * 16777216.0f) * dot + m * qsum;
-#pragma unroll
-      for (int o = 1; o < LPT; o <<= 1) partial += __shfl_xor(partial, o, 64);
+      partial = quad_sum<LPT>(partial);
       if (j == 0 && t < t_end) sc[t - t_begin] = partial * scale_log2;
     }
   }
