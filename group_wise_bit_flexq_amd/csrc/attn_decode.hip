@@ -212,6 +212,29 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   const f16* row = qkv + (int64_t)bi * 3 * h;
   const int64_t slot0 = ((int64_t)(b0 + bi) * nh + head) * kv.max_len;
 
+  const int j = lane % LPT;       // this lane's 32 dims: 32 j .. 32 j + 31 (group j / 2)
+  const int grp = j >> 1;
+  // q and the first batch of K go out before the append: none of these loads can read
+  // position pos unless the first batch reaches it (then the batch waits for the append)
+  uint4 qraw[4];
+  {
+    const uint4* qp = (const uint4*)(row + head * HD + 32 * j);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
+  }
+  uint4 cw[UNR];
+  uint32_t prm[UNR];
+  auto load_k = [&](int tb) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
+      cw[u] = *(const uint4*)(kv.kc + (slot0 + t) * (HD / 2) + 16 * j);
+      prm[u] = kv.kp[(slot0 + t) * GPT + grp];
+    }
+  };
+  const bool k_early = t_begin < t_end && (t_end < T || t_begin + UNR * TPB <= pos);
+  if (k_early) load_k(t_begin);
+
   // ---- 1. quantize-append of this step's k, v at position pos
   if (t_end == T) {
     if (wave == 0) {
@@ -236,18 +259,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   // work-group-scope release/acquire orders the append before the reads below
   __syncthreads();
 
-  // ---- this lane's slice of q: dims 32 j .. 32 j + 31 (group j / 2)
-  const int j = lane % LPT;
-  const int grp = j >> 1;
   // q pairs in the order the K pass forms code pairs: for the 8 dims of word k,
   // qe[2k] = (q0, q2), qe[2k+1] = (q4, q6), qo[2k] = (q1, q3), qo[2k+1] = (q5, q7)
   f16x2 qe[8], qo[8];
   float qsum = 0.0f;
   {
-    const uint4* qp = (const uint4*)(row + head * HD + 32 * j);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 u = qp[c];
+      const uint4 u = qraw[c];
       const f16x2 a = h2_from_u32(u.x), b = h2_from_u32(u.y), cc = h2_from_u32(u.z),
                   d = h2_from_u32(u.w);
       qe[2 * c] = f16x2{a.x, b.x};
@@ -263,14 +282,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   // issued before the first use (token index clamped to the split's last token, the
   // results of clamped lanes discarded), so UNR x 20 B per lane are in flight
   for (int tb = t_begin; tb < t_end; tb += UNR * TPB) {
-    uint4 cw[UNR];
-    uint32_t prm[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
-      cw[u] = *(const uint4*)(kv.kc + (slot0 + t) * (HD / 2) + 16 * j);
-      prm[u] = kv.kp[(slot0 + t) * GPT + grp];
-    }
+    if (!k_early || tb != t_begin) load_k(tb);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int t = tb + u * TPB + wave * TPW + lane / LPT;
@@ -312,6 +324,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     }
   }
 
+  // the dense kernel issues its first batch of V before the softmax statistics
+  const bool v_early = !TOPK && cnt > 0;
+  int rel[UNR];
+  auto load_v = [&](int jb, auto with_list) {
+    constexpr bool LIST = decltype(with_list)::value;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int jj = min(jb + u * TPB + wave * TPW + lane / LPT, cnt - 1);
+      rel[u] = LIST ? (int)list[jj] : jj;
+      const int t = t_begin + rel[u];
+      cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
+      prm[u] = kv.vp[(slot0 + t) * GPT + grp];
+    }
+  };
+  if (v_early) load_v(0, std::false_type{});
+
   // ---- 3. softmax statistics of this split
   float mx = -INFINITY;
   for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
@@ -339,17 +367,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   auto v_pass = [&](auto with_list) {
     constexpr bool LIST = decltype(with_list)::value;
     for (int jb = 0; jb < cnt; jb += UNR * TPB) {
-      uint4 cw[UNR];
-      uint32_t prm[UNR];
-      int rel[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int jj = min(jb + u * TPB + wave * TPW + lane / LPT, cnt - 1);
-        rel[u] = LIST ? (int)list[jj] : jj;
-        const int t = t_begin + rel[u];
-        cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
-        prm[u] = kv.vp[(slot0 + t) * GPT + grp];
-      }
+      if (!v_early || jb != 0) load_v(jb, with_list);
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         // clamped lanes repeat the last position: their weight is zero
