@@ -161,11 +161,9 @@ template <int N>
 __device__ __forceinline__ float quad_sum(float x) {
   static_assert(N == 1 || N == 2 || N == 4, "lanes per token");
   if constexpr (N >= 2)
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
   if constexpr (N >= 4)
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
   return x;
 }
 
@@ -175,8 +173,7 @@ template <int STEP>
 __device__ __forceinline__ float row_sum_stride(float x) {
   if constexpr (STEP < 16) {
     constexpr int kRowRor = 0x120 + STEP;  // DPP row_ror:STEP
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                       0, __builtin_bit_cast(int, x), kRowRor, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kRowRor, 0xF, 0xF, true));
     return row_sum_stride<STEP * 2>(x);
   } else {
     return x;
@@ -278,6 +275,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     }
   }
 
+  // scores in log2 units: the softmax scale folded into the per-token step (with the
+  // 2^24 of the subnormal codes) and into the sum of q for the offset term
+  const float ks = 16777216.0f * scale_log2;
+  const float qsum_s = qsum * scale_log2;
+
   // ---- 2. K pass, UNR block steps per iteration: every load of the iteration is
   // issued before the first use (token index clamped to the split's last token, the
   // results of clamped lanes discarded), so UNR x 20 B per lane are in flight
@@ -302,9 +304,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
       const float dot = __builtin_fmaf(dhi, 0.0625f, dlo);
       const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
       const float s = (float)h_from_bits(prm[u] >> 16);
-      float partial = (s * 16777216.0f) * dot + m * qsum;
+      float partial = (s * ks) * dot + m * qsum_s;
       partial = quad_sum<LPT>(partial);
-      if (j == 0 && t < t_end) sc[t - t_begin] = partial * scale_log2;
+      if (j == 0 && t < t_end) sc[t - t_begin] = partial;
     }
   }
   __syncthreads();
