@@ -212,18 +212,22 @@ extern "C" int flexq_host_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_
   int nt = threads > 0 ? threads : (int)std::thread::hardware_concurrency();
   if (nt < 1) nt = 1;
   if (nt > pairs) nt = (int)pairs;
-  auto work = [&](int w) {
-    std::vector<float> sc((size_t)pos + 1);
-    for (int64_t p = w; p < pairs; p += nt) attend(J, (int)(p / kv->heads), (int)(p % kv->heads), sc.data());
-  };
-  if (nt == 1) {
-    work(0);
-    return FLEXQ_OK;
-  }
+  // every allocation happens here, before any work starts, so nothing can throw
+  // inside a worker and no exception leaves this function
+  std::vector<float> scratch;
   std::vector<std::thread> pool;
+  try {
+    scratch.resize((size_t)nt * ((size_t)pos + 1));
+    pool.reserve(nt - 1);
+  } catch (...) {
+    return FLEXQ_ERR_DEVICE;  // host memory exhausted
+  }
+  auto work = [&](int w) {
+    float* sc = scratch.data() + (size_t)w * ((size_t)pos + 1);
+    for (int64_t p = w; p < pairs; p += nt) attend(J, (int)(p / kv->heads), (int)(p % kv->heads), sc);
+  };
   int started = 1;
   try {
-    pool.reserve(nt - 1);
     for (int w = 1; w < nt; ++w) {
       pool.emplace_back(work, w);
       ++started;

@@ -338,7 +338,9 @@ int flexq_attn_decode_kv4_topk(const uint16_t* qkv, int32_t B, int32_t b0, int32
  * pointer: qkv fp16 [B][3h], out fp16 [B][h], and all arrays of kv (pad included).
  * Runs synchronously on `threads` host threads (<= 0: one per hardware thread),
  * one (sequence, head) pair per thread at a time, so results do not depend on the
- * thread count; returns when done.  No stream, no GPU. */
+ * thread count; returns when done.  No stream, no GPU.  Returns FLEXQ_ERR_DEVICE,
+ * before touching the cache, if the host cannot allocate the threads' score
+ * scratch (nthreads x (pos + 1) floats); fewer threads than asked run the same work. */
 int flexq_host_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
                                const flexq_kv4_layer* kv, uint16_t* out, int32_t threads);
 
