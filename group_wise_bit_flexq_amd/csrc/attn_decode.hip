@@ -208,6 +208,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   const int t_begin = max(split * chunk, npad);
   const f16* row = qkv + (int64_t)bi * 3 * h;
   const int64_t slot0 = ((int64_t)(b0 + bi) * nh + head) * kv.max_len;
+  // raw buffer views of this (sequence, head)'s rows [0, t_end): a load past the end
+  // returns zeros, so the token loops address positions without clamping them
+  const rsrc_t k_rs = make_rsrc(kv.kc + slot0 * (HD / 2), t_end * (HD / 2));
+  const rsrc_t kp_rs = make_rsrc(kv.kp + slot0 * GPT, t_end * GPT * 4);
+  const rsrc_t v_rs = make_rsrc(kv.vc + slot0 * (HD / 2), t_end * (HD / 2));
+  const rsrc_t vp_rs = make_rsrc(kv.vp + slot0 * GPT, t_end * GPT * 4);
 
   const int j = lane % LPT;       // this lane's 32 dims: 32 j .. 32 j + 31 (group j / 2)
   const int grp = j >> 1;
@@ -219,14 +225,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
 #pragma unroll
     for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
   }
-  uint4 cw[UNR];
+  u32x4 cw[UNR];
   uint32_t prm[UNR];
   auto load_k = [&](int tb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int t = min(tb + u * TPB + wave * TPW + lane / LPT, t_end - 1);
-      cw[u] = *(const uint4*)(kv.kc + (slot0 + t) * (HD / 2) + 16 * j);
-      prm[u] = kv.kp[(slot0 + t) * GPT + grp];
+      const int t = tb + u * TPB + wave * TPW + lane / LPT;   // >= t_end: zeros
+      cw[u] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, t * (HD / 2) + 16 * j, 0, 0);
+      prm[u] = __builtin_amdgcn_raw_buffer_load_b32(kp_rs, (t * GPT + grp) * 4, 0, 0);
     }
   };
   const bool k_early = t_begin < t_end && (t_end < T || t_begin + UNR * TPB <= pos);
@@ -281,8 +287,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   const float qsum_s = qsum * scale_log2;
 
   // ---- 2. K pass, UNR block steps per iteration: every load of the iteration is
-  // issued before the first use (token index clamped to the split's last token, the
-  // results of clamped lanes discarded), so UNR x 20 B per lane are in flight
+  // issued before the first use (positions past the split's end read zeros and their
+  // results are discarded), so UNR x 20 B per lane are in flight.  Each lane also
+  // keeps the running maximum of its scores for the softmax.
+  float mx_run = -INFINITY;
   for (int tb = t_begin; tb < t_end; tb += UNR * TPB) {
     if (!k_early || tb != t_begin) load_k(tb);
 #pragma unroll
@@ -306,9 +314,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
       const float s = (float)h_from_bits(prm[u] >> 16);
       float partial = (s * ks) * dot + m * qsum_s;
       partial = quad_sum<LPT>(partial);
+      if (t < t_end) mx_run = fmaxf(mx_run, partial);
       if (j == 0 && t < t_end) sc[t - t_begin] = partial;
     }
   }
+  mx_run = wave_max(mx_run);
+  if (lane == 0) wred[wave] = mx_run;
   __syncthreads();
 
   const int n = t_end - t_begin;   // <= 0 for a split wholly in the padding
@@ -333,22 +344,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     constexpr bool LIST = decltype(with_list)::value;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int jj = min(jb + u * TPB + wave * TPW + lane / LPT, cnt - 1);
-      rel[u] = LIST ? (int)list[jj] : jj;
-      const int t = t_begin + rel[u];
-      cw[u] = *(const uint4*)(kv.vc + (slot0 + t) * (HD / 2) + 16 * j);
-      prm[u] = kv.vp[(slot0 + t) * GPT + grp];
+      const int jr = jb + u * TPB + wave * TPW + lane / LPT;
+      const int jj = min(jr, cnt - 1);
+      rel[u] = LIST ? (int)list[jj] : jj;   // where this lane's p sits in LDS
+      // the position read: past the end (dense walk) the loads return zeros
+      const int t = t_begin + (LIST ? rel[u] : jr);
+      cw[u] = __builtin_amdgcn_raw_buffer_load_b128(v_rs, t * (HD / 2) + 16 * j, 0, 0);
+      prm[u] = __builtin_amdgcn_raw_buffer_load_b32(vp_rs, (t * GPT + grp) * 4, 0, 0);
     }
   };
   if (v_early) load_v(0, std::false_type{});
 
-  // ---- 3. softmax statistics of this split
-  float mx = -INFINITY;
-  for (int i = tid; i < n; i += 256) mx = fmaxf(mx, sc[i]);
-  mx = wave_max(mx);
-  if (lane == 0) wred[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  // ---- 3. softmax statistics of this split (the maximum comes from the K pass; a
+  // top-k cut keeps the largest score, so the maximum is the same)
+  const float mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
   float ls = 0.0f;
   for (int i = tid; i < n; i += 256) {
     const float p = exp2f(sc[i] - mx);
