@@ -267,6 +267,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   f16x2 qe[8], qo[8];
   float qsum = 0.0f;
   {
+    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 u = qraw[c];
@@ -276,8 +277,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
       qe[2 * c + 1] = f16x2{cc.x, d.x};
       qo[2 * c] = f16x2{a.y, b.y};
       qo[2 * c + 1] = f16x2{cc.y, d.y};
-      qsum += (((float)a.x + (float)a.y) + ((float)b.x + (float)b.y)) +
-              (((float)cc.x + (float)cc.y) + ((float)d.x + (float)d.y));
+      qsum = __builtin_amdgcn_fdot2(a, ones, qsum, false);   // q * 1 is exact
+      qsum = __builtin_amdgcn_fdot2(b, ones, qsum, false);
+      qsum = __builtin_amdgcn_fdot2(cc, ones, qsum, false);
+      qsum = __builtin_amdgcn_fdot2(d, ones, qsum, false);
     }
   }
 
@@ -360,7 +363,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   const float mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
   float ls = 0.0f;
   for (int i = tid; i < n; i += 256) {
-    const float p = exp2f(sc[i] - mx);
+    // v_exp_f32 as is: arguments are <= 0, and only weights below 2^-126 (nothing
+    // next to the maximum's 1) lose their subnormal tail
+    const float p = __builtin_amdgcn_exp2f(sc[i] - mx);
     sc[i] = p;
     ls += p;
   }
