@@ -706,7 +706,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
 
   f16x8 fbc[3], fbn[3];   // B fragments: this / next k-step
   uint32_t cw0, cw1, cw2, pw0, pw1, pw2, t0, t1;
-  f16x2 s2, m2;
+  f16x2 sp[3], mp[3];   // (scale, scale) and (offset, offset) of the 3 columns' group
   f32x4 acc[MT16][3];
 #pragma unroll
   for (int i = 0; i < MT16; ++i)
@@ -727,19 +727,25 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
     cw0 = *(const uint32_t*)((ST) + c_off + 16 * (WORD));         \
     cw1 = *(const uint32_t*)((ST) + c_off + 512 + 16 * (WORD));   \
     cw2 = *(const uint32_t*)((ST) + c_off + 1024 + 16 * (WORD));  \
-    pw0 = *(const uint32_t*)((ST) + p_off);                       \
-    pw1 = *(const uint32_t*)((ST) + p_off + 64);                  \
-    pw2 = *(const uint32_t*)((ST) + p_off + 128);                 \
+    if ((WORD) == 0) {                                            \
+      pw0 = *(const uint32_t*)((ST) + p_off);                     \
+      pw1 = *(const uint32_t*)((ST) + p_off + 64);                \
+      pw2 = *(const uint32_t*)((ST) + p_off + 128);               \
+    }                                                             \
   } while (0)
-#define DEQ(F, t, CW, PW)                                                           \
+// word 0 of a k-tile (one 64-element group) expands the group's scale and offset into
+// fp16 pairs; word 1 reuses them
+#define DEQ(F, t, CW, PW, WORD)                                                     \
   do {                                                                              \
-    s2 = h2_from_u32(((PW) >> 16) * 0x10001u);                                      \
-    m2 = h2_from_u32(((PW) & 0xFFFFu) * 0x10001u);                                  \
+    if ((WORD) == 0) {                                                              \
+      sp[t] = h2_from_u32(((PW) >> 16) * 0x10001u);                                 \
+      mp[t] = h2_from_u32(((PW) & 0xFFFFu) * 0x10001u);                             \
+    }                                                                               \
     w4_word_to_bytes(CW, t0, t1);                                                   \
-    const f16x2 _d0 = dequant_pair(code_pair_f16<false>(t0), s2, m2);               \
-    const f16x2 _d1 = dequant_pair(code_pair_f16<true>(t0), s2, m2);                \
-    const f16x2 _d2 = dequant_pair(code_pair_f16<false>(t1), s2, m2);               \
-    const f16x2 _d3 = dequant_pair(code_pair_f16<true>(t1), s2, m2);                \
+    const f16x2 _d0 = dequant_pair(code_pair_f16<false>(t0), sp[t], mp[t]);         \
+    const f16x2 _d1 = dequant_pair(code_pair_f16<true>(t0), sp[t], mp[t]);          \
+    const f16x2 _d2 = dequant_pair(code_pair_f16<false>(t1), sp[t], mp[t]);         \
+    const f16x2 _d3 = dequant_pair(code_pair_f16<true>(t1), sp[t], mp[t]);          \
     F[t] = (f16x8){_d0[0], _d0[1], _d1[0], _d1[1], _d2[0], _d2[1], _d3[0], _d3[1]}; \
   } while (0)
 // one k-step: MT16 x 3 MFMAs with B fragments FB, A fragments read one row tile ahead;
@@ -759,9 +765,9 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
       acc[_i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[2], acc[_i][2], 0, 0, 0);   \
       SB();                                                                                   \
       if (_i == 0) READ_W(WST, WORD);                                                         \
-      if (_i == 1) DEQ(FN, 0, cw0, pw0);                                                      \
-      if (_i == 2) DEQ(FN, 1, cw1, pw1);                                                      \
-      if (_i == 3) DEQ(FN, 2, cw2, pw2);                                                      \
+      if (_i == 1) DEQ(FN, 0, cw0, pw0, WORD);                                                \
+      if (_i == 2) DEQ(FN, 1, cw1, pw1, WORD);                                                \
+      if (_i == 3) DEQ(FN, 2, cw2, pw2, WORD);                                                \
       SB();                                                                                   \
     }                                                                                         \
   } while (0)
@@ -790,9 +796,9 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
     DEC_WAIT_VM(S::SLOTS * (NST - 2));
     DEC_BARRIER();
     READ_W(st0, 0);
-    DEQ(fbc, 0, cw0, pw0);
-    DEQ(fbc, 1, cw1, pw1);
-    DEQ(fbc, 2, cw2, pw2);
+    DEQ(fbc, 0, cw0, pw0, 0);
+    DEQ(fbc, 1, cw1, pw1, 0);
+    DEQ(fbc, 2, cw2, pw2, 0);
     // whole groups of NST k-tiles, then the 0..NST-1 left over (starting on stage 0);
     // (a break after every k-tile makes the compiler spill the accumulators)
     for (; kt + NST - 1 <= klast;) {
