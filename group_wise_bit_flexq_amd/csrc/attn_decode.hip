@@ -11,10 +11,14 @@
 //  2. K pass: score_t = sum_g [ s_g * sum_d q_d c_td + m_g * sum_d q_d ]  (the
 //     dequantized key c*s+m never materialises).  Codes enter v_dot2_f32_f16 as fp16
 //     subnormals c * 2^-24, so every product is exact and the 2^24 is folded into s;
-//  3. softmax over the split in fp32 (two passes over scores kept in LDS);
-//  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs;
+//  3. softmax over the split in fp32: the maximum is kept during the K pass, then one
+//     pass over the scores in LDS turns them into weights and sums them;
+//  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs fed two exact fp16
+//     codes per convert;
 //  5. with several splits, each writes (max, sum, o[]) and a merge kernel rescales
 //     and adds them in split order.
+// The K and V rows of one (sequence, head) are read through raw buffer views that end
+// at the split's last position, so lanes past the end read zeros and are discarded.
 // Left padding: positions below the sequence's pad count are never read; a split that
 // lies wholly below it writes an empty partial (max -inf, sum 0), which the merge
 // weights by 0 (the split holding pos is never empty).
@@ -386,7 +390,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
       if (!v_early || jb != 0) load_v(jb, with_list);
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        // clamped lanes repeat the last position: their weight is zero
+        // lanes past the end of the walk: weight zero (their loads read zeros, or
+        // repeat the last kept position)
         const bool live = jb + u * TPB + wave * TPW + lane / LPT < cnt;
         const float p = live ? sc[rel[u]] : 0.0f;
         const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
@@ -473,7 +478,7 @@ struct DecPlan {
 };
 
 // Unroll of the token loops: the largest of 4, 3, 2 that wastes at most 1/8 of the
-// block steps of a split on clamped lanes, else 1.
+// block steps of a split on lanes past its end, else 1.
 static int dec_unroll(int steps) {
   for (int u = 4; u >= 2; --u)
     if (((steps + u - 1) / u * u - steps) * 8 <= steps) return u;
@@ -491,7 +496,7 @@ static DecPlan dec_plan(int B, int heads, int head_dim, int pos) {
   chunk = (chunk + step - 1) / step * step;
   if (chunk > kDecMaxChunk) chunk = kDecMaxChunk;
   const int nsplit = (T + chunk - 1) / chunk;
-  // the longest split decides; shorter (last) splits only clamp more lanes
+  // the longest split decides; a shorter (last) split only has more lanes past its end
   DecPlan p{nsplit, chunk, dec_unroll((std::min(chunk, T) + step - 1) / step)};
   return p;
 }
