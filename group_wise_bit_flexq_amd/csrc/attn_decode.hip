@@ -247,18 +247,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     if (wave == 0) {
       const int gi = min(lane >> 3, 2 * GPT - 1);
       const int sub = lane & 7;
-      const int isv = gi / GPT, grp = gi % GPT;
-      const f16x8 xv = *(const f16x8*)(row + (1 + isv) * h + head * HD + grp * 64 + sub * 8);
+      const int isv = gi / GPT, ag = gi % GPT;   // K or V, group within the head
+      const f16x8 xv = *(const f16x8*)(row + (1 + isv) * h + head * HD + ag * 64 + sub * 8);
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = (float)xv[e];
       uint32_t packed[1];
-      const uint32_t prm = GroupQ<8>::run(x, packed);
+      const uint32_t aprm = GroupQ<8>::run(x, packed);
       if ((lane >> 3) < 2 * GPT) {
         uint8_t* cb = isv ? kv.vc : kv.kc;
         uint32_t* pb = isv ? kv.vp : kv.kp;
-        *(uint32_t*)(cb + (slot0 + pos) * (HD / 2) + grp * 32 + sub * 4) = packed[0];
-        if (sub == 0) pb[(slot0 + pos) * GPT + grp] = prm;
+        *(uint32_t*)(cb + (slot0 + pos) * (HD / 2) + ag * 32 + sub * 4) = packed[0];
+        if (sub == 0) pb[(slot0 + pos) * GPT + ag] = aprm;
       }
     }
   }
