@@ -385,7 +385,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float pm = 0.0f;
   auto v_pass = [&](auto with_list) {
-    constexpr bool LIST = decltype(with_list)::value;
     for (int jb = 0; jb < cnt; jb += UNR * TPB) {
       if (!v_early || jb != 0) load_v(jb, with_list);
 #pragma unroll

@@ -108,7 +108,7 @@ struct HostSplit {
   uint16_t *qkv, *out;        // pinned host staging
 };
 
-int run_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t h, int32_t ffn,
+int run_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t h,
               const uint16_t* x_in, int64_t rows, bool prefill, int32_t nb, int32_t S,
               int32_t b0, int32_t pos, uint16_t* x_out, const LayerScratch& s,
               hipStream_t stream, flexq_trace* tr = nullptr, float sparsity = 0.0f,
@@ -263,7 +263,7 @@ extern "C" int flexq_prefill_layer(const flexq_layer* L, const flexq_kv4_layer* 
   LayerScratch s;
   const size_t need = layer_carve((char*)ws, hidden, heads, ffn, rows, 0, &s);
   if (!ws || ws_bytes < need) return FLEXQ_ERR_INVALID;
-  return run_layer(L, kv, hidden, ffn, x_in, rows, true, nb, S, b0, 0, x_out, s, stream);
+  return run_layer(L, kv, hidden, x_in, rows, true, nb, S, b0, 0, x_out, s, stream);
 }
 
 extern "C" int flexq_decode_layer(const flexq_layer* L, const flexq_kv4_layer* kv, int32_t hidden,
@@ -276,7 +276,7 @@ extern "C" int flexq_decode_layer(const flexq_layer* L, const flexq_kv4_layer* k
   LayerScratch s;
   const size_t need = layer_carve((char*)ws, hidden, heads, ffn, B, pos + 1, &s);
   if (!ws || ws_bytes < need) return FLEXQ_ERR_INVALID;
-  return run_layer(L, kv, hidden, ffn, x_in, B, false, B, 1, b0, pos, x_out, s, stream);
+  return run_layer(L, kv, hidden, x_in, B, false, B, 1, b0, pos, x_out, s, stream);
 }
 
 extern "C" size_t flexq_model_workspace_size(int32_t hidden, int32_t heads, int32_t ffn,
@@ -345,11 +345,11 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
     if (host_rows) {  // K/V through the device stage, then to the host tier
-      TRY(run_layer(&m->layer[l], &stage, m->hidden, m->ffn, x, rows, true, nb, S, 0, 0, y, ls,
+      TRY(run_layer(&m->layer[l], &stage, m->hidden, x, rows, true, nb, S, 0, 0, y, ls,
                     stream, m->trace));
       TRY(stage_to_host(stage, ht->kv[l], b0 - ht->row0, stream));
     } else {
-      TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, rows, true, nb, S, b0, 0, y,
+      TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, x, rows, true, nb, S, b0, 0, y,
                     ls, stream, m->trace));
     }
     std::swap(x, y);
@@ -385,7 +385,7 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
     if (nhost > 0)
       hs = HostSplit{&ht->kv[l], ht->row0, ht->threads, (uint16_t*)ht->host_ws,
                      (uint16_t*)ht->host_ws + (size_t)nhost * 3 * m->hidden};
-    TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, m->ffn, x, B, false, B, 1, 0, pos, y, ls,
+    TRY(run_layer(&m->layer[l], &m->kv[l], m->hidden, x, B, false, B, 1, 0, pos, y, ls,
                   stream, m->trace, m->attn_sparsity, nhost > 0 ? &hs : nullptr));
     std::swap(x, y);
   }
