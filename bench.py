@@ -13,6 +13,15 @@ generated on the device, quantized once with flexq_quantize (load time, not time
 Prints one JSON line.  `roofline` is measured live: HIP events bracket every prefill
 4-bit GEMM launch of the timed steps on the stream they run on.  `cpu_baseline`
 times the oracle on a bounded sample of the same workload and extrapolates.
+
+Run length.  A step of the OPT-175B workload is a whole generation (about 20 s on
+one MI355X), so --steps and --warmup are upper bounds: after the first warm-up step
+the run keeps as many further warm-up steps as fit in a quarter of --budget-s and as
+many timed steps as fit in --budget-s (at least one).  The JSON line reports the
+counts actually run (`steps`, `warmup`) next to the requested ones.
+
+--graph captures each decode step (one graph per position) in a HIP graph once,
+outside the timed region, and replays them inside it; prefill runs eagerly.
 """
 from __future__ import annotations
 
@@ -45,6 +54,10 @@ def parse():
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--budget-s", type=float, default=90.0,
+                    help="wall-clock seconds the timed steps may take (caps --steps)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the decode steps from HIP graphs captured once")
     return ap.parse_args()
 
 
@@ -105,29 +118,49 @@ def build_model(wl, seed, F, synth, workloads):
     return model
 
 
-def generate(model, wl, tokens, out, trace_ptr=None, events=None):
+def generate(model, wl, tokens, out, trace_ptr=None, events=None, graphs=None):
     """One step: prefill per micro-batch, then gen-1 decode steps over the whole batch.
 
-    events: optional three torch.cuda.Events recorded at start / end of prefill / end."""
-    import torch
+    out: int32 [gen][batch]; row i receives the i-th generated token of every sequence
+    (decode step i reads row i - 1 and writes row i in place, so nothing is copied).
+    events: optional three torch.cuda.Events recorded at start / end of prefill / end.
+    graphs: optional HIP graphs of the decode steps (see capture_decode)."""
     mb, S = wl.micro_batch, wl.prompt
-    first = torch.empty(wl.batch, dtype=torch.int32, device=tokens.device)
     if events:
         events[0].record()
     model._struct.trace = trace_ptr
     for j in range(wl.batch // mb):
-        model.prefill(tokens[j * mb:(j + 1) * mb], b0=j * mb, next_out=first[j * mb:(j + 1) * mb])
+        model.prefill(tokens[j * mb:(j + 1) * mb], b0=j * mb, next_out=out[0, j * mb:(j + 1) * mb])
     model._struct.trace = None
     if events:
         events[1].record()
-    out[:, 0].copy_(first)
-    cur = first
     for i in range(wl.gen - 1):
-        nxt = model.decode_step(cur, S + i)
-        out[:, i + 1].copy_(nxt)
-        cur = nxt
+        if graphs:
+            graphs[i].replay()
+        else:
+            model.decode_step(out[i], S + i, next_out=out[i + 1])
     if events:
         events[2].record()
+
+
+def capture_decode(model, wl, out):
+    """One HIP graph per decode position: step i reads out[i], writes out[i + 1]."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(wl.gen - 1):      # eager once, so every kernel is loaded
+            model.decode_step(out[i], wl.prompt + i, next_out=out[i + 1])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i in range(wl.gen - 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            model.decode_step(out[i], wl.prompt + i, next_out=out[i + 1])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
 
 
 def decode_bytes(wl):
@@ -248,33 +281,57 @@ def main():
     model = build_model(wl, args.seed, F, synth, workloads)
     tokens = synth.token_ids(wl.batch, wl.prompt, wl.vocab, synth.sub_seed(args.seed, "tokens"))
     tokens = tokens.cuda()
-    out = torch.empty(wl.batch, wl.gen, dtype=torch.int32, device="cuda")
+    out = torch.empty(wl.gen, wl.batch, dtype=torch.int32, device="cuda")
+    graphs = None
+    if args.graph:
+        t = time.perf_counter()
+        generate(model, wl, tokens, out)     # fills the caches the captured steps read
+        graphs = capture_decode(model, wl, out)
+        log(f"captured {len(graphs)} decode-step graphs ({time.perf_counter() - t:.1f}s)")
+
+    # warm-up: the first step measures the step time, the rest fit in budget / 4
+    warm, step_s = 0, None
+    t_w = time.perf_counter()
+    while warm < args.warmup:
+        t = time.perf_counter()
+        generate(model, wl, tokens, out, graphs=graphs)
+        torch.cuda.synchronize()
+        step_s = time.perf_counter() - t
+        warm += 1
+        log(f"warmup {warm}/{args.warmup} done ({step_s:.2f}s)")
+        if time.perf_counter() - t_w + step_s > 0.25 * args.budget_s:
+            break
+    steps = max(1, min(args.steps, int(args.budget_s // step_s))) if step_s else args.steps
+    if steps < args.steps:
+        log(f"timing {steps} of {args.steps} requested steps ({step_s:.1f}s each, "
+            f"budget {args.budget_s:.0f}s)")
 
     # trace of the prefill linears (events recorded by the library on its stream)
     n_mb = wl.batch // wl.micro_batch
-    cap = n_mb * (wl.layers * 4 + 1) * max(1, args.steps)
+    cap = n_mb * (wl.layers * 4 + 1) * steps
     ev = hip.events(2 * cap)
     kinds = (C.c_int32 * cap)()
     rows = (C.c_int64 * cap)()
     trace = F.TraceStruct(C.cast(ev, C.POINTER(C.c_void_p)), kinds, rows, cap, 0)
 
-    for i in range(args.warmup):
-        generate(model, wl, tokens, out)
-        torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{args.warmup} done")
-
-    stream = torch.cuda.current_stream()
-    e_pre = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    e_pre = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        generate(model, wl, tokens, out, C.pointer(trace), events=e_pre[3 * s:3 * s + 3])
-        log(f"step {s + 1}/{args.steps} enqueued")
+    done = 0
+    while done < steps:
+        generate(model, wl, tokens, out, C.pointer(trace), events=e_pre[3 * done:3 * done + 3],
+                 graphs=graphs)
+        done += 1
+        log(f"step {done}/{steps} enqueued")
+        if step_s is None:        # no warm-up: the first timed step sets the count
+            torch.cuda.synchronize()
+            step_s = time.perf_counter() - t0
+            steps = max(1, min(steps, int(args.budget_s // step_s)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prefill_ms = sum(e_pre[3 * s].elapsed_time(e_pre[3 * s + 1]) for s in range(args.steps))
-    decode_ms = sum(e_pre[3 * s + 1].elapsed_time(e_pre[3 * s + 2]) for s in range(args.steps))
-    log(f"timed {args.steps} step(s): wall {wall:.2f}s prefill {prefill_ms / 1e3:.2f}s "
+    prefill_ms = sum(e_pre[3 * s].elapsed_time(e_pre[3 * s + 1]) for s in range(steps))
+    decode_ms = sum(e_pre[3 * s + 1].elapsed_time(e_pre[3 * s + 2]) for s in range(steps))
+    log(f"timed {steps} step(s): wall {wall:.2f}s prefill {prefill_ms / 1e3:.2f}s "
         f"decode {decode_ms / 1e3:.2f}s")
 
     # dominant kernel: the prefill 4-bit GEMM (every linear of a prefill micro-batch)
@@ -292,17 +349,24 @@ def main():
     achieved = gemm_flop / (gemm_ms / 1e3) / 1e12 if gemm_ms > 0 else 0.0
     traffic = traffic_from_profiles(wl)
 
-    gen_tokens = wl.batch * wl.gen * args.steps
+    gen_tokens = wl.batch * wl.gen * steps
     value = gen_tokens / wall
-    dec_gbps = decode_bytes(wl) * args.steps / (decode_ms / 1e3) / 1e9
+    dec_gbps = decode_bytes(wl) * steps / (decode_ms / 1e3) / 1e9
+    metric = "generated tokens/s, OPT-175B-shape W4+KV4 batch 144; decode HBM GB/s vs peak"
+    if wl.name != "opt175b":
+        metric = (f"generated tokens/s, {wl.name}-shape W4+KV4 batch {wl.batch}; "
+                  "decode HBM GB/s vs peak")
     res = {
-        "metric": "generated tokens/s, OPT-175B-shape W4+KV4 batch 144; decode HBM GB/s vs peak",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 2),
+        "steps": steps,
+        "warmup": warm,
+        "steps_requested": args.steps,
+        "warmup_requested": args.warmup,
+        "budget_s": args.budget_s,
+        "ms_per_step": round(wall * 1e3 / steps, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(value / PAGES_TOKS_PER_S, 2) if wl.name == "opt175b" else None,
@@ -317,9 +381,10 @@ def main():
             "seq_len": wl.prompt,
             "gen_len": wl.gen,
             "parallelism": "single GPU",
+            "decode_graphs": bool(graphs),
         },
-        "prefill_s": round(prefill_ms / 1e3 / args.steps, 3),
-        "decode_s": round(decode_ms / 1e3 / args.steps, 3),
+        "prefill_s": round(prefill_ms / 1e3 / steps, 3),
+        "decode_s": round(decode_ms / 1e3 / steps, 3),
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {
