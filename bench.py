@@ -90,34 +90,6 @@ class Hip:
             self.lib.hipEventDestroy(C.c_void_p(e))
 
 
-def build_model(wl, seed, F, synth, workloads):
-    import torch
-    dev = "cuda"
-    h, f, nh = wl.hidden, wl.ffn, wl.heads
-    layers = []
-    t0 = time.time()
-    for l in range(wl.layers):
-        w16 = synth.layer_weights_fp16(h, f, seed, l, device=dev)
-        layers.append(F.QLayer.from_fp16(w16, nh, dev))
-        del w16
-        if (l + 1) % 16 == 0 or l + 1 == wl.layers:
-            torch.cuda.synchronize()
-            log(f"built layer {l + 1}/{wl.layers} ({time.time() - t0:.1f}s)")
-    emb16 = synth.model_tensor("embed", (wl.vocab, h), seed, dev)
-    emb = F.quantize_weight(emb16)
-    del emb16
-    pos = synth.model_tensor("pos", (workloads.POS_ROWS, h), seed, dev)
-    lnf_g = synth.model_tensor("lnf_g", (h,), seed, dev)
-    lnf_b = synth.model_tensor("lnf_b", (h,), seed, dev)
-    model = F.QModel(layers, emb, pos, lnf_g, lnf_b, nh, wl.batch, wl.max_len,
-                     wl.micro_batch * wl.prompt, dev)
-    torch.cuda.synchronize()
-    log(f"model ready: weights {model.weight_bytes() / 1e9:.1f} GB, KV4 "
-        f"{sum(c.nbytes() for c in model.caches) / 1e9:.1f} GB, workspace "
-        f"{model.workspace.numel() / 1e9:.1f} GB")
-    return model
-
-
 def generate(model, wl, tokens, out, trace_ptr=None, events=None, graphs=None):
     """One step: prefill per micro-batch, then gen-1 decode steps over the whole batch.
 
@@ -278,7 +250,7 @@ def main():
     F.lib()
     hip = Hip()
     log(f"workload {wl}")
-    model = build_model(wl, args.seed, F, synth, workloads)
+    model = workloads.build_model(wl, args.seed, log=log)
     tokens = synth.token_ids(wl.batch, wl.prompt, wl.vocab, synth.sub_seed(args.seed, "tokens"))
     tokens = tokens.cuda()
     out = torch.empty(wl.gen, wl.batch, dtype=torch.int32, device="cuda")

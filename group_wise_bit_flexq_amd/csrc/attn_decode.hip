@@ -540,9 +540,9 @@ extern "C" size_t flexq_attn_decode_workspace_size(int32_t B, int32_t heads, int
   return (size_t)B * heads * p.splits * (head_dim + 2) * sizeof(float);
 }
 
-extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
-                                     const flexq_kv4_layer* kv, uint16_t* out, void* ws,
-                                     size_t ws_bytes, hipStream_t stream) {
+// Argument checks of dense decode attention (everything but the workspace).
+static int check_decode_args(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                             const flexq_kv4_layer* kv, const uint16_t* out) {
   if (!kv || !qkv || !out) return FLEXQ_ERR_INVALID;
   if (B < 0 || b0 < 0 || pos < 0) return FLEXQ_ERR_INVALID;
   if (B == 0) return FLEXQ_OK;
@@ -554,9 +554,14 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
       ((uintptr_t)kv->pad & 3))
     return FLEXQ_ERR_INVALID;
   if (kv->heads > 65535 || B > 65535) return FLEXQ_ERR_UNSUPPORTED;
+  return FLEXQ_OK;
+}
+
+// Launches the dense decode (and the merge when the context is split) with the split
+// partials in ws (checked by the caller: at least the workspace size, 16-byte aligned).
+static int run_decode(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                      const flexq_kv4_layer* kv, uint16_t* out, void* ws, hipStream_t stream) {
   const DecPlan p = dec_plan(B, kv->heads, kv->head_dim, pos);
-  const size_t need = flexq_attn_decode_workspace_size(B, kv->heads, kv->head_dim, pos);
-  if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15))) return FLEXQ_ERR_INVALID;
   KVViewD v{kv->k_codes, kv->v_codes, (uint32_t*)kv->k_params, (uint32_t*)kv->v_params, kv->heads,
             kv->max_len};
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
@@ -576,6 +581,16 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   }
   FLEXQ_LAUNCH_CHECK();
   return FLEXQ_OK;
+}
+
+extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                                     const flexq_kv4_layer* kv, uint16_t* out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  const int st = check_decode_args(qkv, B, b0, pos, kv, out);
+  if (st != FLEXQ_OK || B == 0) return st;
+  const size_t need = flexq_attn_decode_workspace_size(B, kv->heads, kv->head_dim, pos);
+  if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15))) return FLEXQ_ERR_INVALID;
+  return run_decode(qkv, B, b0, pos, kv, out, ws, stream);
 }
 
 extern "C" int flexq_attn_decode_kv4_topk(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,

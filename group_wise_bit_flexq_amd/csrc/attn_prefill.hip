@@ -25,6 +25,7 @@
 // Left padding (the generation loop's attention mask): keys below the sequence's pad
 // count are masked, key blocks wholly below it are skipped (except the work-group's
 // own two, which the store needs staged), and a query with no visible key writes 0.
+#include "host_cache.h"
 #include "quant_dev.h"
 
 namespace flexq {
@@ -321,13 +322,12 @@ extern "C" int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int
   const int64_t items = (int64_t)((S + 127) / 128) * kv->heads * B;
   if (items > 0x7FFFFFFF) return FLEXQ_ERR_UNSUPPORTED;
   dim3 grid((unsigned)items);
-  static bool attr_set = false;   // 72 KB of LDS for head_dim 128: above the default limit
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)attn_prefill_kernel<128>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)PrefillShape<128>::LDS_BYTES);
-    attr_set = true;
-  }
+  static PerDeviceInt attr_set;   // 72 KB of LDS for head_dim 128: above the default limit
+  (void)attr_set.get([] {
+    return hipFuncSetAttribute((const void*)attn_prefill_kernel<128>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)PrefillShape<128>::LDS_BYTES) == hipSuccess ? 1 : 0;
+  }, 0);
   if (kv->head_dim == 64)
     hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), PrefillShape<64>::LDS_BYTES, stream,
                        (const f16*)qkv, S, kv->heads, b0, v, kv->pad, (f16*)out, scale_log2);

@@ -863,6 +863,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 // ------------------------------------------------------------------ host dispatch
 
+}  // namespace flexq
+
+#include "host_cache.h"
+
+namespace flexq {
+
 struct Plan {
   int cfg;      // which kernel / tile shape
   int bm, bn;
@@ -874,43 +880,42 @@ constexpr int kCfgBig = 0;      // M > 160: 256 x 256 tile, 8 waves (pipelined, 
 constexpr int kCfgSkinny = 1;   // M <= 64 or 144 < M <= 160: 32*ceil(M/32) x 256 tile
 constexpr int kCfgDec = 2;      // 64 < M <= 144: 16*ceil(M/16) x 384 tile, 8 waves
 
-// Work-groups of the small-M kernel that one device runs at once (occupancy x CUs),
-// cached per device and tile height.
+// Work-groups of the small-M kernels that one device runs at once (occupancy x CUs),
+// looked up once per device and tile height.
 template <int MT>
 static int skinny_blocks_per_cu() {
-  static int n = 0;
-  if (n == 0) {
+  static PerDeviceInt cache;
+  return cache.get([] {
     int b = 0;
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b, gemm_w4_skinny_kernel<MT, 4, 2, kOutPartial>, 256, SkinnyShape<MT, 4, 2>::LDS_BYTES);
-    n = b > 0 ? b : 1;
-  }
-  return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &b, gemm_w4_skinny_kernel<MT, 4, 2, kOutPartial>, 256,
+            SkinnyShape<MT, 4, 2>::LDS_BYTES) != hipSuccess)
+      return 0;
+    return b;
+  }, 1);
 }
 
 template <int MT16>
 static int dec_blocks_per_cu() {
-  static int n = 0;
-  if (n == 0) {
+  static PerDeviceInt cache;
+  return cache.get([] {
     int b = 0;
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &b, gemm_w4_dec_kernel<MT16, kOutPartial>, 512, 0);
-    n = b > 0 ? b : 1;
-  }
-  return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gemm_w4_dec_kernel<MT16, kOutPartial>,
+                                                     512, 0) != hipSuccess)
+      return 0;
+    return b;
+  }, 1);
 }
 
 static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  const int slot = dev >= 0 && dev < 64 ? dev : 0;
-  if (cus[slot] == 0) {
-    int n = 0;
-    (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    cus[slot] = n > 0 ? n : 256;
-  }
-  return cus[slot];
+  static PerDeviceInt cache;
+  return cache.get([] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }, 256);
 }
 
 static int64_t dec_concurrency(int mt16) {
@@ -985,12 +990,11 @@ static void launch_big(const Plan& p, const f16* x, const flexq_w4* W, int M, Ep
                        void* Y, hipStream_t stream) {
   using S = GemmShape<WM, WN, TM, TN>;
   auto kern = gemm_w4_big_kernel<WM, WN, TM, TN, OUT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)S::LDS_BYTES);
-    attr_set = true;
-  }
+  static PerDeviceInt attr_set;   // the dynamic LDS limit, raised once per device
+  (void)attr_set.get([&] {
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)S::LDS_BYTES) == hipSuccess ? 1 : 0;
+  }, 0);
   const int N = (int)W->rows, K = (int)W->cols;
   const int tiles = ((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
   dim3 grid(tiles, p.splits);

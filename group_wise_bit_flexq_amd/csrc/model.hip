@@ -184,6 +184,29 @@ size_t model_carve(char* base, int32_t h, int32_t heads, int32_t ffn, int32_t vo
   return c.used;
 }
 
+// Validates the model's tap against a call of `rows` rows.
+int check_tap(const flexq_model* m, int64_t rows) {
+  const flexq_tap* t = m->tap;
+  if (!t || t->count == 0) return FLEXQ_OK;
+  if (t->count < 0 || !t->layers || !t->x || rows > t->rows_cap) return FLEXQ_ERR_INVALID;
+  for (int i = 0; i < t->count; ++i)
+    if (t->layers[i] < 0 || t->layers[i] > m->layers || !t->x[i]) return FLEXQ_ERR_INVALID;
+  return FLEXQ_OK;
+}
+
+// Copies the hidden state x (rows x hidden) entering layer l (l == layers: the
+// output head) into every tap buffer that names l.
+int tap_copy(const flexq_model* m, int l, const uint16_t* x, int64_t rows, hipStream_t stream) {
+  const flexq_tap* t = m->tap;
+  if (!t) return FLEXQ_OK;
+  for (int i = 0; i < t->count; ++i)
+    if (t->layers[i] == l &&
+        hipMemcpyAsync(t->x[i], x, (size_t)rows * m->hidden * 2, hipMemcpyDeviceToDevice,
+                       stream) != hipSuccess)
+      return FLEXQ_ERR_DEVICE;
+  return FLEXQ_OK;
+}
+
 int check_model(const flexq_model* m) {
   if (!m || m->layers <= 0 || !m->layer || !m->kv || !m->pos || !m->lnf_g || !m->lnf_b)
     return FLEXQ_ERR_INVALID;
@@ -332,6 +355,7 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
     return FLEXQ_ERR_INVALID;   // also a micro-batch that straddles the host tier
   }
   const int64_t rows = (int64_t)nb * S;
+  TRY(check_tap(m, rows));
   ModelScratch s;
   TRY(model_scratch(m, rows, nb, 0, &s));
   const int32_t* pad = m->kv[0].pad;
@@ -344,6 +368,7 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
   const flexq_kv4_layer stage = host_rows ? stage_view(m, nb, b0) : flexq_kv4_layer{};
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
+    TRY(tap_copy(m, l, x, rows, stream));
     if (host_rows) {  // K/V through the device stage, then to the host tier
       TRY(run_layer(&m->layer[l], &stage, m->hidden, x, rows, true, nb, S, 0, 0, y, ls,
                     stream, m->trace));
@@ -354,6 +379,7 @@ extern "C" int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_
     }
     std::swap(x, y);
   }
+  TRY(tap_copy(m, m->layers, x, rows, stream));
   return model_head(m, x + (int64_t)(S - 1) * m->hidden, (int64_t)S * m->hidden, nb, b0, S - 1,
                     true, next, logits, s, stream);
 }
@@ -371,6 +397,7 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
     if (!ht->host_ws || ht->host_ws_bytes < (size_t)nhost * 4 * m->hidden * 2)
       return FLEXQ_ERR_INVALID;
   }
+  TRY(check_tap(m, B));
   ModelScratch s;
   TRY(model_scratch(m, B, B, pos + 1, &s));
   TRY(flexq_embed(tokens, B, pos, 1, m->kv[0].pad, &m->embed, m->pos, m->pos_rows, s.x0,
@@ -381,6 +408,7 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
   uint16_t* y = s.x1;
   for (int l = 0; l < m->layers; ++l) {
     TRY(check_layer_args(&m->layer[l], &m->kv[l], m->hidden, m->heads, m->ffn));
+    TRY(tap_copy(m, l, x, B, stream));
     HostSplit hs{};
     if (nhost > 0)
       hs = HostSplit{&ht->kv[l], ht->row0, ht->threads, (uint16_t*)ht->host_ws,
@@ -389,5 +417,6 @@ extern "C" int flexq_decode_step(const flexq_model* m, const int32_t* tokens, in
                   stream, m->trace, m->attn_sparsity, nhost > 0 ? &hs : nullptr));
     std::swap(x, y);
   }
+  TRY(tap_copy(m, m->layers, x, B, stream));
   return model_head(m, x, m->hidden, B, 0, pos, false, next, logits, s, stream);
 }

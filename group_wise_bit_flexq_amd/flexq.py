@@ -24,6 +24,7 @@ EXPORTED = (
     "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4", "flexq_host_stage_size",
     "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
+    "flexq_probe_mfma",
 )
 
 
@@ -75,6 +76,12 @@ class HostTierStruct(C.Structure):
                 ("stage", C.c_void_p), ("stage_bytes", C.c_size_t)]
 
 
+class TapStruct(C.Structure):
+    """flexq_tap: copies of the hidden state entering listed layers."""
+    _fields_ = [("count", C.c_int32), ("layers", C.POINTER(C.c_int32)),
+                ("x", C.POINTER(C.c_void_p)), ("rows_cap", C.c_int64)]
+
+
 class ModelStruct(C.Structure):
     _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("heads", C.c_int32),
                 ("ffn", C.c_int32), ("vocab", C.c_int32), ("pos_rows", C.c_int32),
@@ -83,7 +90,8 @@ class ModelStruct(C.Structure):
                 ("lnf_b", C.c_void_p), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_size_t), ("trace", C.POINTER(TraceStruct)),
                 ("gen", C.POINTER(GenConfig)), ("stopped", C.c_void_p),
-                ("attn_sparsity", C.c_float), ("host", C.POINTER(HostTierStruct))]
+                ("attn_sparsity", C.c_float), ("host", C.POINTER(HostTierStruct)),
+                ("tap", C.POINTER(TapStruct))]
 
 
 _lib = None
@@ -131,6 +139,7 @@ def lib():
             "flexq_model_workspace_size": (sz, [i32, i32, i32, i32, i64, i32, i32]),
             "flexq_prefill": (C.c_int, [C.POINTER(ModelStruct), vp, i32, i32, i32, vp, vp, vp]),
             "flexq_decode_step": (C.c_int, [C.POINTER(ModelStruct), vp, i32, i32, vp, vp, vp]),
+            "flexq_probe_mfma": (C.c_int, [i32, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -464,6 +473,14 @@ def embed(tokens, pos_base, seq, emb: W4, pos_table, out=None, stream=None, pad=
     return y
 
 
+def probe_mfma(mode, blocks, iters, out=None, stream=None):
+    """Matrix-core rate probe (flexq_probe_mfma): returns the checksum tensor."""
+    y = out if out is not None else torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    _check("flexq_probe_mfma", lib().flexq_probe_mfma(int(mode), int(blocks), int(iters),
+                                                      y.data_ptr(), _stream(stream)))
+    return y
+
+
 def argmax(logits, out=None, stream=None):
     M, N = logits.shape
     y = out if out is not None else torch.empty(M, dtype=torch.int32, device=logits.device)
@@ -606,6 +623,24 @@ class QModel:
                                         self.host_ws.data_ptr(), self.host_ws.numel() * 2,
                                         self.stage.data_ptr(), sb)
             self._struct.host = C.pointer(self._host)
+
+    def set_tap(self, layers=None, rows=0):
+        """Copy the hidden state entering each listed layer (len(layers) = the output
+        head's input) on every following prefill / decode call of up to `rows` rows;
+        returns the device buffers [rows][hidden], in the order of `layers`.  None
+        removes the tap."""
+        if not layers:
+            self._tap = self._tap_bufs = None
+            self._struct.tap = None
+            return []
+        dev = self.workspace.device
+        self._tap_bufs = [torch.empty(rows, self.hidden, dtype=torch.float16, device=dev)
+                          for _ in layers]
+        self._tap_layers = (C.c_int32 * len(layers))(*layers)
+        self._tap_ptrs = (C.c_void_p * len(layers))(*[b.data_ptr() for b in self._tap_bufs])
+        self._tap = TapStruct(len(layers), self._tap_layers, self._tap_ptrs, rows)
+        self._struct.tap = C.pointer(self._tap)
+        return self._tap_bufs
 
     def set_attn_sparsity(self, sparsity=0.0):
         """Decode attention keeps each query's ceil(sparsity * n) best positions when

@@ -30,6 +30,10 @@
     python -m group_wise_bit_flexq_amd.kernel_probe pick --workload opt175b --reps 5
         the token choice of one decode step (batch x vocab fp32 logits): greedy, and
         temperature sampling with a stop token;
+    python -m group_wise_bit_flexq_amd.kernel_probe mfma --reps 3
+        the matrix cores' sustained fp16 rate (v_mfma_f32_32x32x16_f16 streams, two waves
+        per SIMD on every CU) with constant, fixed random and changing random operands:
+        the ceiling the GEMMs' TFLOP/s are read against;
     python -m group_wise_bit_flexq_amd.kernel_probe copy --mib 1024 --reps 3
         an elementwise device copy of a known size, the reference that scales the
         HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above, and a
@@ -287,6 +291,21 @@ def pick(wl, reps):
     return res
 
 
+def mfma(reps, iters=20000):
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flop = blocks * 4 * iters * 4 * 32768.0          # 4 waves x iters x 4 MFMAs x 32x32x16x2
+    res = {"cus": cus, "blocks": blocks, "iters": iters}
+    for mode, name in ((0, "constant"), (1, "random_fixed"), (2, "random_changing")):
+        ms = _time(lambda: F.probe_mfma(mode, blocks, iters, out=out), reps)
+        res[name] = {"ms": ms, "tflops": flop / ms / 1e9}
+    return res
+
+
 def copy(mib, reps):
     import torch
     n = mib * (1 << 20) // 2
@@ -300,7 +319,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["gemm", "decode", "sparse", "host_attn", "host_tier",
                                      "prefill_attn", "quant", "quant_ex", "stress", "pick",
-                                     "copy"])
+                                     "mfma", "copy"])
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
@@ -330,6 +349,8 @@ def main():
         r = stress(a.reps)
     elif a.what == "pick":
         r = pick(wl, a.reps)
+    elif a.what == "mfma":
+        r = mfma(a.reps)
     else:
         r = copy(a.mib, a.reps)
     print(json.dumps({"probe": a.what, "workload": a.workload, "results": r}), flush=True)

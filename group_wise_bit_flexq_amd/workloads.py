@@ -55,3 +55,40 @@ KV_STRESS = dict(batch=64, heads=56, head_dim=128, prompt=2048, steps=64,
                  outlier_frac=0.01, outlier_factor=8.0)
 # standalone quantize of a 4 GiB fp16 tensor (2^31 elements)
 QUANT_4GIB = dict(rows=524288, cols=4096)
+
+
+def build_model(wl: Workload, seed: int = 0, device="cuda", log=None):
+    """The OPT-shaped model of a full-model workload with synthetic weights (every
+    tensor drawn on the device from its per-tensor seed, matrices and the embedding
+    quantized there): the model the benchmark times and the full-size parity tests
+    check.  log: None, or a function taking one status line."""
+    import time
+
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    h, f, nh = wl.hidden, wl.ffn, wl.heads
+    layers = []
+    t0 = time.time()
+    for l in range(wl.layers):
+        w16 = synth.layer_weights_fp16(h, f, seed, l, device=device)
+        layers.append(F.QLayer.from_fp16(w16, nh, device))
+        del w16
+        if log and ((l + 1) % 16 == 0 or l + 1 == wl.layers):
+            torch.cuda.synchronize()
+            log(f"built layer {l + 1}/{wl.layers} ({time.time() - t0:.1f}s)")
+    emb16 = synth.model_tensor("embed", (wl.vocab, h), seed, device)
+    emb = F.quantize_weight(emb16)
+    del emb16
+    pos = synth.model_tensor("pos", (POS_ROWS, h), seed, device)
+    lnf_g = synth.model_tensor("lnf_g", (h,), seed, device)
+    lnf_b = synth.model_tensor("lnf_b", (h,), seed, device)
+    model = F.QModel(layers, emb, pos, lnf_g, lnf_b, nh, wl.batch, wl.max_len,
+                     wl.micro_batch * wl.prompt, device)
+    torch.cuda.synchronize()
+    if log:
+        log(f"model ready: weights {model.weight_bytes() / 1e9:.1f} GB, KV4 "
+            f"{sum(c.nbytes() for c in model.caches) / 1e9:.1f} GB, workspace "
+            f"{model.workspace.numel() / 1e9:.1f} GB")
+    return model

@@ -14,8 +14,12 @@
  *     `stream` and return without waiting.  A rejected call enqueues nothing.
  *     A launch failure reported by the runtime returns FLEXQ_ERR_DEVICE; a fault
  *     inside a kernel surfaces at the caller's next synchronisation.
- *   - No global state: calls on distinct streams and buffers may run concurrently.
- *   - Results are deterministic: fixed reduction and merge orders.
+ *   - No state is kept between calls except host-side, per-device caches of launch
+ *     facts (occupancy, CU count, raised LDS limits), looked up once per device and
+ *     published atomically.  Calls on distinct streams and buffers may run
+ *     concurrently, from any thread.
+ *   - Results are deterministic: fixed reduction and merge orders, chosen from the
+ *     shapes, the workspace size and the device's CU count and occupancy only.
  *
  * Compressed formats (FlexGen source walkthrough, section 6.3: num_bits 4,
  * group_size 64, asymmetric; weights grouped along group_dim 0, the cache along
@@ -186,6 +190,21 @@ typedef struct {
 
 size_t flexq_host_stage_size(int32_t heads, int32_t head_dim, int32_t nb, int32_t max_len);
 
+/* Optional copies of the hidden states between layers, for checking a whole run
+ * layer by layer (the engine's layer loop of source notes "Flex Opt" keeps each
+ * layer's input and output in one hidden buffer; a tap copies that buffer out).
+ * When a model carries a tap, flexq_prefill and flexq_decode_step copy, on their
+ * stream, the input of layer layers[i] (all rows of the call, rows x hidden fp16)
+ * into x[i]; layers[i] == the model's layer count names the last layer's output
+ * (the input of the final LayerNorm).  A call with more rows than rows_cap, or a
+ * layer index outside [0, layers], returns FLEXQ_ERR_INVALID before any work. */
+typedef struct {
+  int32_t count;
+  const int32_t* layers; /* HOST [count] */
+  uint16_t* const* x;    /* HOST [count] of DEVICE buffers, rows_cap * hidden fp16 each */
+  int64_t rows_cap;
+} flexq_tap;
+
 /* A whole OPT-shaped model.  Non-owning: every pointer stays the caller's.
  * `layer` and `kv` are HOST arrays of `layers` entries (the structs inside hold
  * device pointers).  embed is the 4-bit token embedding [vocab][hidden], also used
@@ -216,6 +235,8 @@ typedef struct {
   /* NULL, or a HOST host-tier description (see flexq_host_tier); not combined with
    * sparse attention */
   const flexq_host_tier* host;
+  /* NULL, or a HOST tap description (see flexq_tap) */
+  const flexq_tap* tap;
 } flexq_model;
 
 const char* flexq_status_string(int status);
@@ -272,19 +293,35 @@ int flexq_dequantize(const uint8_t* codes, const uint16_t* params, int64_t rows,
                      uint16_t* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- LayerNorm
+ * The layer norms of the OPT decoder stack (source notes, "Flex Opt": the model is an
+ * embedding, N transformer layers and an output head; the pages name the layers but
+ * not their norm, so this follows the OPT architecture: pre-LN twice per layer and a
+ * final norm before the head).
  * y[m] = (x[m] - mean) / sqrt(biased var + 1e-5) * g + b, statistics in fp32,
  * fp16 out.  Row m of x starts at x + m * x_row_stride (elements); y is dense
- * [M][h].  h a multiple of 8. */
+ * [M][h].  h a multiple of 8 up to FLEXQ_LN_MAX_HIDDEN, the stride a multiple of 8
+ * and >= h, x, g, b, y 16-byte aligned and not NULL, M >= 0 (M = 0 does nothing);
+ * anything else -> FLEXQ_ERR_INVALID. */
+#define FLEXQ_LN_MAX_HIDDEN 16384
 int flexq_layernorm(const uint16_t* x, int64_t M, int64_t h, int64_t x_row_stride,
                     const uint16_t* g, const uint16_t* b, uint16_t* y, hipStream_t stream);
 
 /* ---------------------------------------------------------------- 4-bit linear
- * y[M][N] = fp16( [relu](x . W^T + bias) [+ residual] ), W = fp16-dequantized
- * 4-bit weight [N][K] (the pages' fp16 linear layers with compressed weights).
- * x fp16 [M][K]; bias fp16 [N] or NULL; residual fp16 [M][N] or NULL (may equal
- * y); relu 0/1.  fp16 MFMA operands, fp32 accumulation, one rounding at the end.
- * K a multiple of 64.  ws: scratch for split-K partial sums, at least
- * flexq_linear_w4_workspace_size(M, N, K) bytes (may be 0 -> NULL allowed). */
+ * A linear layer of the decoder with its weight compressed group-wise (walkthrough
+ * section 6.3: weights compressed to 4 bits in groups of 64 along group_dim 0, the
+ * input dimension, and decompressed to the original fp16 for the layer's matmul;
+ * source notes "Pytorch Backend": a compressed weight is the (codes, scale, shape)
+ * triple that the backend decompresses before use).  Here the decompression happens
+ * inside the GEMM's tiles and the weight is never materialised:
+ * y[M][N] = fp16( [relu](x . W^T + bias) [+ residual] ), W = the fp16 value
+ * fp16(code * scale + offset) of every 4-bit weight [N][K] (one rounding).
+ * x fp16 [M][K] (16-byte aligned); bias fp16 [N] or NULL; residual fp16 [M][N] or
+ * NULL (may equal y); relu 0/1.  fp16 MFMA operands, fp32 accumulation, one rounding
+ * at the end.  K a multiple of 64, else FLEXQ_ERR_INVALID.  ws: scratch for split-K
+ * partial sums (16-byte aligned); flexq_linear_w4_workspace_size(M, N, K) bytes give
+ * the fastest split; a smaller workspace (NULL and 0 included) is accepted and runs
+ * with as many splits as fit (fewer or none): the same error bound, another (fixed)
+ * summation order. */
 size_t flexq_linear_w4_workspace_size(int64_t M, int64_t N, int64_t K);
 int flexq_linear_w4(const uint16_t* x, int64_t M, const flexq_w4* W, const uint16_t* bias,
                     const uint16_t* residual, int32_t relu, uint16_t* y, void* ws,
@@ -298,8 +335,11 @@ int flexq_linear_w4_f32(const uint16_t* x, int64_t M, const flexq_w4* W, float* 
 /* ---------------------------------------------------------------- attention
  * Prefill attention (source notes, "Pytorch Backend": `mha`).  qkv fp16
  * [B*S][3h], rows ordered (b, t).  For each sequence and head: causal
- * softmax(q k^T / sqrt(head_dim)) v over the fp16 K/V of this pass (fp32 scores
- * and softmax), output fp16 out [B*S][h].  K and V of the S positions are then
+ * softmax(q k^T / sqrt(head_dim)) v over the fp16 K/V of this pass, output fp16
+ * out [B*S][h].  Scores, their maximum and the softmax sums are fp32; the
+ * probabilities multiply V as fp16 MFMA operands (each p in [0, 1] rounded once to
+ * fp16, relative error <= 2^-11) with fp32 accumulation, so the output may differ
+ * from an all-fp32 softmax by up to about 2^-11 max|v| beyond the final rounding.  K and V of the S positions are then
  * quantized into cache rows b0 .. b0+B-1, positions [0, S).  Needs
  * b0 + B <= kv->batch and S <= kv->max_len. */
 int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int32_t b0,
@@ -398,8 +438,13 @@ size_t flexq_model_workspace_size(int32_t hidden, int32_t heads, int32_t ffn, in
 int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32_t S, int32_t b0,
                   int32_t* next, float* logits, hipStream_t stream);
 
-/* One decode step of B sequences (cache rows 0..B-1): tokens int32 [B]
- * at position pos -> next [B] (and logits [B][vocab] if not NULL).  Without a
+/* One decode step of B sequences (walkthrough section 4.1, `generate`: after the
+ * prompt, each step feeds every sequence's last token through the model and picks
+ * the next; source notes "Flex Opt": per step the engine walks the layers, loading
+ * and storing each layer's cache around its compute).  Cache rows 0..B-1: tokens
+ * int32 [B] at position pos -> next [B] (and logits [B][vocab] if not NULL).  The
+ * token is embedded at position pos - pad of its row, each layer appends its k, v at
+ * cache position pos (quantized) and attends over [pad, pos].  Without a
  * host tier the call neither synchronises nor allocates, so a caller may capture
  * it in a HIP graph (pos and the generation config are baked into the captured
  * kernels); with host rows it waits on the stream once per layer (see
@@ -408,6 +453,15 @@ int flexq_prefill(const flexq_model* m, const int32_t* tokens, int32_t nb, int32
  * FLEXQ_ERR_UNSUPPORTED. */
 int flexq_decode_step(const flexq_model* m, const int32_t* tokens, int32_t B, int32_t pos,
                       int32_t* next, float* logits, hipStream_t stream);
+
+/* ---------------------------------------------------------------- measurement aid
+ * Not part of the decoder path: the sustained rate of the fp16 matrix cores, the
+ * ceiling the GEMMs are measured against.  `blocks` work-groups of 256 threads (two
+ * per CU) each stream 4 * iters v_mfma_f32_32x32x16_f16 per wave (32768 flop each)
+ * on independent accumulators; mode 0 constant operands, 1 fixed pseudo-random fp16
+ * operands, 2 the same with their mantissa bits changed every iteration.  out: device
+ * float [blocks * 256] (a checksum per thread).  Bad arguments -> FLEXQ_ERR_INVALID. */
+int flexq_probe_mfma(int32_t mode, int32_t blocks, int32_t iters, float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

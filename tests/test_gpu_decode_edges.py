@@ -54,3 +54,73 @@ def test_decode_first_batch_at_the_appended_position(hd, batch_positions):
     vmax = 15 * 0.1 + np.abs(oc.v_params[..., 0].astype(np.float64)).max()
     for b in range(B):
         assert_close_fp16(out[b], ref[b], extra=2.0**-16 * vmax, what=f"seq {b} pad {pads[b]}")
+
+
+def _edge_groups(rng, n):
+    """n fp16 64-groups covering the quantizer's special cases: constant, all-zero
+    (with -0), a step that underflows fp16, a -0 minimum, exact ties (step 1, values
+    on k + 1/2), the largest finite range, and ordinary N(0, 1) groups."""
+    out = np.empty((n, 64))
+    for i in range(n):
+        kind = i % 7
+        if kind == 0:
+            out[i] = rng.choice([3.25, -7.5, 1024.0])
+        elif kind == 1:
+            out[i] = 0.0
+        elif kind == 2:
+            out[i] = rng.integers(0, 3, size=64) * 2.0**-24
+        elif kind == 3:
+            out[i] = np.abs(rng.normal(size=64))
+            out[i, rng.integers(0, 64)] = 0.0          # made -0 below
+        elif kind == 4:
+            lo = rng.choice([0.0, -8.0, 32.0])
+            out[i] = lo + rng.integers(0, 15, size=64) + 0.5
+            out[i, 0], out[i, 1] = lo, lo + 15.0
+        elif kind == 5:
+            out[i] = rng.uniform(-60000, 60000, size=64)
+            out[i, 0], out[i, 1] = -65504.0, 65504.0
+        else:
+            out[i] = rng.normal(size=64)
+    x = out.astype(F16)
+    x[3::7][x[3::7] == 0] = F16(-0.0)
+    x[1::7][:, ::2] = F16(-0.0)
+    return x
+
+
+@pytest.mark.parametrize("B,nh,hd,pos", [(2, 4, 64, 300), (2, 4, 128, 300),
+                                         (8, 128, 64, 40), (8, 128, 128, 40)])
+def test_decode_append_edge_groups(B, nh, hd, pos):
+    """The token's k and v, quantized by the decode kernel at position pos (by the last
+    context split when the context is split, B x heads < 1024), equal the oracle's codes
+    and (offset, scale) bit for bit on every special group; outputs stay in the bound."""
+    F = require_gpu()
+    T = pos + 1
+    _say("decode append edges", B, nh, hd, pos)
+    rng = np.random.default_rng(B * nh + hd + pos)
+    h = nh * hd
+    oc = O.KVCache(B, nh, hd, T)
+    kv = F.KV4(B, nh, hd, T)
+    prev = rng.normal(size=(B, nh, pos, hd)).astype(F16)
+    for b in range(B):
+        oc.store(b, 0, prev[b], prev[b])
+    for name in ("k_codes", "v_codes", "k_params", "v_params"):
+        getattr(kv, name).copy_(torch.from_numpy(getattr(oc, name)))
+    q1 = (rng.normal(size=(B, 3 * h)) * 0.05).astype(F16)
+    q1[:, h:2 * h] = _edge_groups(rng, B * h // 64).reshape(B, h)
+    q1[:, 2 * h:] = _edge_groups(rng, B * h // 64).reshape(B, h)
+    q1[:, 2 * h:][np.abs(q1[:, 2 * h:].astype(np.float64)) > 1e3] *= F16(1e-3)   # keep |v| modest
+    out = to_np(F.attn_decode(torch.from_numpy(q1).cuda(), pos, kv))
+    torch.cuda.synchronize()
+    ref = O.attn_decode(q1, pos, oc)
+    for name in ("k_codes", "v_codes", "k_params", "v_params"):
+        a, b = to_np(getattr(kv, name))[:, :, pos], getattr(oc, name)[:, :, pos]
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), name
+    # bound: the kernel's own 2^-16 max|v| plus the fp32 score error (hd 2^-23 sum|q||k|,
+    # large where a K group spans the whole fp16 range) carried through the softmax
+    q = q1[:, :h].astype(np.float64).reshape(B, nh, hd)
+    kd = O.dequantize_kv(oc.k_codes, oc.k_params)             # [B][nh][T][hd]
+    vmax = np.abs(O.dequantize_kv(oc.v_codes, oc.v_params)).max(axis=(2, 3))
+    sabs = np.einsum("bhtd,bhd->bht", np.abs(kd), np.abs(q)).max(axis=2) / np.sqrt(hd)
+    delta = hd * 2.0**-23 * sabs
+    extra = (vmax * (2.0**-16 + 4 * delta))[:, :, None] * np.ones((1, 1, hd))
+    assert_close_fp16(out, ref, extra=extra.reshape(B, h), what="decode over edge groups")

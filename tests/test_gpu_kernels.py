@@ -31,6 +31,10 @@ def _groups_mix(rng, rows, cols):
     g *= np.where(((sel >= 0.10) & (sel < 0.4))[..., None], scale, 1.0)
     out = rng.random(g.shape) < 0.01
     g[out] *= 8
+    ties = (sel >= 0.4) & (sel < 0.45)           # step exactly 1, values on k + 1/2
+    k = rng.integers(0, 15, size=(ties.sum(), 64)) + 0.5
+    k[:, 0], k[:, 1] = 0.0, 15.0
+    g[ties] = k + rng.choice([0.0, -8.0, 32.0], size=(ties.sum(), 1))
     x = g.reshape(rows, cols).astype(F16)
     negz = rng.random(x.shape) < 0.02
     x[negz & (x == 0)] = F16(-0.0)
