@@ -183,9 +183,14 @@ def test_tiny_model_greedy():
 
 @pytest.mark.timeout(900)
 def test_opt13b_greedy_sampled():
+    """OPT-1.3B shape, batch 32: eight sequences spread over the batch, all 32 tokens,
+    teacher-forced.  A sequence with no near-tie generates, free-running, exactly the
+    oracle's tokens (each of its steps fed the same history gave the same argmax)."""
     F = require_gpu()
     wl = WORKLOADS["opt1.3b"]
-    _say("opt1.3b greedy, sampled sequences 0 and 31")
+    sample = [0, 4, 9, 13, 18, 22, 27, 31]
+    _say("opt1.3b greedy, sampled sequences", sample)
     parts = _host_model(wl.hidden, wl.heads, wl.ffn, wl.vocab, wl.layers, 0)
-    _greedy_check(F, parts, wl.heads, B=wl.batch, S=wl.prompt, G=wl.gen, mb=wl.micro_batch,
-                  sample=[0, 31])
+    ties = _greedy_check(F, parts, wl.heads, B=wl.batch, S=wl.prompt, G=wl.gen,
+                         mb=wl.micro_batch, sample=sample)
+    assert ties <= 0.1 * len(sample) * wl.gen, f"{ties} near-tie differences"
