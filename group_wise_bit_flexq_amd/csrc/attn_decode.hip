@@ -27,8 +27,10 @@
 // order-preserving 32-bit keys, equal keys ranked by position), the others become
 // -inf, and the V pass walks a compacted list of the kept positions only.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
+#include "host_cache.h"
 #include "quant_dev.h"
 
 namespace flexq {
@@ -583,6 +585,29 @@ static int run_decode(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
   return FLEXQ_OK;
 }
 
+// The split partials of flexq_attn_decode_kv4_static: a static array that every device
+// the library runs on holds until the process ends.  In host code `scratch` only
+// stands for the symbol; its address on a device comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in scratch_ptr.
+static __device__ __align__(256) float scratch[FLEXQ_STATIC_SCRATCH_BYTES / sizeof(float)];
+static std::atomic<void*> scratch_ptr[kMaxDevices];
+
+static int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FLEXQ_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FLEXQ_ERR_UNSUPPORTED;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FLEXQ_ERR_DEVICE;
+    }
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return FLEXQ_OK;
+}
+
 extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
                                      const flexq_kv4_layer* kv, uint16_t* out, void* ws,
                                      size_t ws_bytes, hipStream_t stream) {
@@ -590,6 +615,21 @@ extern "C" int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0,
   if (st != FLEXQ_OK || B == 0) return st;
   const size_t need = flexq_attn_decode_workspace_size(B, kv->heads, kv->head_dim, pos);
   if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15))) return FLEXQ_ERR_INVALID;
+  return run_decode(qkv, B, b0, pos, kv, out, ws, stream);
+}
+
+extern "C" int flexq_attn_decode_kv4_static(const uint16_t* qkv, int32_t B, int32_t b0,
+                                            int32_t pos, const flexq_kv4_layer* kv,
+                                            uint16_t* out, hipStream_t stream) {
+  const int st = check_decode_args(qkv, B, b0, pos, kv, out);
+  if (st != FLEXQ_OK || B == 0) return st;
+  const size_t need = flexq_attn_decode_workspace_size(B, kv->heads, kv->head_dim, pos);
+  if (need > FLEXQ_STATIC_SCRATCH_BYTES) return FLEXQ_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int sst = static_scratch(&ws);
+    if (sst != FLEXQ_OK) return sst;
+  }
   return run_decode(qkv, B, b0, pos, kv, out, ws, stream);
 }
 

@@ -21,7 +21,8 @@ EXPORTED = (
     "flexq_dequantize", "flexq_dequantize_ex", "flexq_layernorm",
     "flexq_linear_w4_workspace_size", "flexq_linear_w4", "flexq_linear_w4_f32",
     "flexq_attn_prefill", "flexq_attn_decode_workspace_size", "flexq_attn_decode_kv4",
-    "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4", "flexq_host_stage_size",
+    "flexq_attn_decode_kv4_static", "flexq_attn_decode_kv4_topk", "flexq_host_attn_decode_kv4",
+    "flexq_host_stage_size",
     "flexq_embed", "flexq_argmax", "flexq_pick", "flexq_layer_workspace_size", "flexq_prefill_layer",
     "flexq_decode_layer", "flexq_model_workspace_size", "flexq_prefill", "flexq_decode_step",
     "flexq_probe_mfma",
@@ -122,6 +123,8 @@ def lib():
             "flexq_attn_decode_workspace_size": (sz, [i32, i32, i32, i32]),
             "flexq_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct), vp, vp,
                                                 sz, vp]),
+            "flexq_attn_decode_kv4_static": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
+                                                       vp, vp]),
             "flexq_attn_decode_kv4_topk": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),
                                                      C.c_float, vp, vp]),
             "flexq_host_attn_decode_kv4": (C.c_int, [vp, i32, i32, i32, C.POINTER(KV4Struct),

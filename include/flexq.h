@@ -356,6 +356,25 @@ int flexq_attn_decode_kv4(const uint16_t* qkv, int32_t B, int32_t b0, int32_t po
                           const flexq_kv4_layer* kv, uint16_t* out, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Decode attention that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation, kernels and result bits as flexq_attn_decode_kv4,
+ * with the context-split partials in a static device array of
+ * FLEXQ_STATIC_SCRATCH_BYTES that each device holds from the call's first use on it
+ * until the process ends (its address is looked up once per device).  Needs
+ * flexq_attn_decode_workspace_size(B, heads, head_dim, pos) <=
+ * FLEXQ_STATIC_SCRATCH_BYTES (4 MiB; the size is 0 when B x heads >= 1024 and
+ * pos < 4096, and at most about 1.1 MB when B x heads < 1024 and pos + 1 <=
+ * 2^22 / (B x heads)), else FLEXQ_ERR_UNSUPPORTED before any work;
+ * FLEXQ_ERR_DEVICE if the array's device address cannot be obtained.  Every call on
+ * one device shares that device's array: calls that overlap in time on one device
+ * (two streams, two threads) race on it and must be ordered by the caller.  Each
+ * call writes every partial it reads, so nothing carries over from a previous call
+ * and nothing needs clearing. */
+#define FLEXQ_STATIC_SCRATCH_BYTES (4u << 20)
+int flexq_attn_decode_kv4_static(const uint16_t* qkv, int32_t B, int32_t b0, int32_t pos,
+                                 const flexq_kv4_layer* kv, uint16_t* out, hipStream_t stream);
+
 /* Sparse decode attention (source notes "Flex Opt": the `attn_sparsity` policy, whose
  * mechanism the pages leave open).  As flexq_attn_decode_kv4, except that each query
  * keeps only the k = max(1, ceil(min(sparsity, 1) * n)) highest of its n scores
