@@ -705,6 +705,8 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
   } while (0)
 
   f16x8 fbc[3], fbn[3];   // B fragments: this / next k-step
+  constexpr bool kPf2 = MT16 % 3 == 0;
+  f16x8 af[3];            // A fragments two row tiles ahead (kPf2)
   uint32_t cw0, cw1, cw2, pw0, pw1, pw2, t0, t1;
   f16x2 sp[3], mp[3];   // (scale, scale) and (offset, offset) of the 3 columns' group
   f32x4 acc[MT16][3];
@@ -748,27 +750,48 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
     const f16x2 _d3 = dequant_pair(code_pair_f16<true>(t1), sp[t], mp[t]);          \
     F[t] = (f16x8){_d0[0], _d0[1], _d1[0], _d1[1], _d2[0], _d2[1], _d3[0], _d3[1]}; \
   } while (0)
-// one k-step: MT16 x 3 MFMAs with B fragments FB, A fragments read one row tile ahead;
-// after the MFMAs of row tile i: i = 0 reads code words WORD of stage WST, i = 1..3
-// dequantize them into FN
+// one k-step: MT16 x 3 MFMAs with B fragments FB; after the MFMAs of row tile i: i = 0
+// reads code words WORD of stage WST, i = 1..3 dequantize them into FN.  A fragments:
+// when MT16 is a multiple of 3, row tile r of every k-step sits in af[r % 3], read two
+// row tiles ahead, and the first two row tiles of the next k-step (k-step WORD of
+// stage WST: this stage's k-step 1, or the next stage's k-step 0, whose loads the wait
+// at the top of the k-tile has covered) are read during the last two row tiles of
+// this one, so no k-step starts by waiting for LDS; otherwise one row tile ahead.
 #define KSTEP(ST, KS, FB, FN, WST, WORD)                                                      \
   do {                                                                                        \
-    f16x8 _a0 = FRAG_A(ST, KS, 0), _a1 = _a0;                                                 \
-    _Pragma("unroll") for (int _i = 0; _i < MT16; ++_i) {                                    \
-      if (_i + 1 < MT16) {                                                                    \
-        if (_i & 1) _a0 = FRAG_A(ST, KS, _i + 1);                                             \
-        else _a1 = FRAG_A(ST, KS, _i + 1);                                                    \
+    if constexpr (kPf2) {                                                                     \
+      _Pragma("unroll") for (int _i = 0; _i < MT16; ++_i) {                                  \
+        if (_i + 2 < MT16) af[(_i + 2) % 3] = FRAG_A(ST, KS, _i + 2);                         \
+        else af[(_i + 2) % 3] = FRAG_A(WST, WORD, _i + 2 - MT16);                             \
+        const f16x8 _a = af[_i % 3];                                                          \
+        acc[_i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[0], acc[_i][0], 0, 0, 0); \
+        acc[_i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[1], acc[_i][1], 0, 0, 0); \
+        acc[_i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[2], acc[_i][2], 0, 0, 0); \
+        SB();                                                                                 \
+        if (_i == 0) READ_W(WST, WORD);                                                       \
+        if (_i == 1) DEQ(FN, 0, cw0, pw0, WORD);                                              \
+        if (_i == 2) DEQ(FN, 1, cw1, pw1, WORD);                                              \
+        if (_i == 3) DEQ(FN, 2, cw2, pw2, WORD);                                              \
+        SB();                                                                                 \
       }                                                                                       \
-      const f16x8 _a = (_i & 1) ? _a1 : _a0;                                                  \
-      acc[_i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[0], acc[_i][0], 0, 0, 0);   \
-      acc[_i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[1], acc[_i][1], 0, 0, 0);   \
-      acc[_i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[2], acc[_i][2], 0, 0, 0);   \
-      SB();                                                                                   \
-      if (_i == 0) READ_W(WST, WORD);                                                         \
-      if (_i == 1) DEQ(FN, 0, cw0, pw0, WORD);                                                \
-      if (_i == 2) DEQ(FN, 1, cw1, pw1, WORD);                                                \
-      if (_i == 3) DEQ(FN, 2, cw2, pw2, WORD);                                                \
-      SB();                                                                                   \
+    } else {                                                                                  \
+      f16x8 _a0 = FRAG_A(ST, KS, 0), _a1 = _a0;                                               \
+      _Pragma("unroll") for (int _i = 0; _i < MT16; ++_i) {                                  \
+        if (_i + 1 < MT16) {                                                                  \
+          if (_i & 1) _a0 = FRAG_A(ST, KS, _i + 1);                                           \
+          else _a1 = FRAG_A(ST, KS, _i + 1);                                                  \
+        }                                                                                     \
+        const f16x8 _a = (_i & 1) ? _a1 : _a0;                                                \
+        acc[_i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[0], acc[_i][0], 0, 0, 0); \
+        acc[_i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[1], acc[_i][1], 0, 0, 0); \
+        acc[_i][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(_a, FB[2], acc[_i][2], 0, 0, 0); \
+        SB();                                                                                 \
+        if (_i == 0) READ_W(WST, WORD);                                                       \
+        if (_i == 1) DEQ(FN, 0, cw0, pw0, WORD);                                              \
+        if (_i == 2) DEQ(FN, 1, cw1, pw1, WORD);                                              \
+        if (_i == 3) DEQ(FN, 2, cw2, pw2, WORD);                                              \
+        SB();                                                                                 \
+      }                                                                                       \
     }                                                                                         \
   } while (0)
 // k-tile kt on stage ST (NXT: the stage of kt + 1, FREE: the stage of kt - 1, which
@@ -799,6 +822,10 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_dec_kernel(
     DEQ(fbc, 0, cw0, pw0, 0);
     DEQ(fbc, 1, cw1, pw1, 0);
     DEQ(fbc, 2, cw2, pw2, 0);
+    if constexpr (kPf2) {
+      af[0] = FRAG_A(st0, 0, 0);
+      af[1] = FRAG_A(st0, 0, 1);
+    }
     // whole groups of NST k-tiles, then the 0..NST-1 left over (starting on stage 0);
     // (a break after every k-tile makes the compiler spill the accumulators)
     for (; kt + NST - 1 <= klast;) {

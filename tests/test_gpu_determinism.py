@@ -22,6 +22,7 @@ def _say(*a):
 
 
 @pytest.mark.parametrize("M,N,K", [(144, 1024, 8192),    # decode kernel, split-K
+                                   (144, 33792, 4096),   # decode kernel, two splits
                                    (32, 512, 8192),      # small-M kernel, split-K
                                    (512, 512, 4096),     # large-M kernel, split-K (few tiles)
                                    (1000, 768, 2048)])   # large-M kernel, no split
