@@ -148,11 +148,11 @@ def decode_bytes(wl):
 
 def gemm_source_hash():
     """Hash of the device code the prefill GEMM is built from: common.h and gemm_w4.hip
-    up to its host-dispatch section (host-side planning changes do not invalidate
-    counters taken on the kernel)."""
+    up to its small-M kernels (changes to the decode kernels or to host-side planning
+    do not invalidate counters taken on the prefill kernel)."""
     csrc = os.path.join(ROOT, "group_wise_bit_flexq_amd", "csrc")
     gemm = open(os.path.join(csrc, "gemm_w4.hip"), "rb").read()
-    cut = gemm.find(b"// ------------------------------------------------------------------ host dispatch")
+    cut = gemm.find(b"// ------------------------------------------------------------------ small-M kernel")
     body = open(os.path.join(csrc, "common.h"), "rb").read() + (gemm[:cut] if cut >= 0 else gemm)
     return hashlib.sha256(body).hexdigest()[:16]
 
