@@ -250,10 +250,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
       const int gi = min(lane >> 3, 2 * GPT - 1);
       const int sub = lane & 7;
       const int isv = gi / GPT, ag = gi % GPT;   // K or V, group within the head
-      const f16x8 xv = *(const f16x8*)(row + (1 + isv) * h + head * HD + ag * 64 + sub * 8);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)xv[e];
+      const f16x8 x[1] = {*(const f16x8*)(row + (1 + isv) * h + head * HD + ag * 64 + sub * 8)};
       uint32_t packed[1];
       const uint32_t aprm = GroupQ<8>::run(x, packed);
       if ((lane >> 3) < 2 * GPT) {

@@ -281,12 +281,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
       xa = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch));
       xb = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch + 1));
     }
-    float x[16];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = (float)xa[e];
-      x[8 + e] = (float)xb[e];
-    }
+    const f16x8 x[2] = {xa, xb};
     uint32_t packed[2];
     const uint32_t prm = GroupQ<4>::run(x, packed);
     if (tok < S) {

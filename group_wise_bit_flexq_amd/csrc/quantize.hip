@@ -31,14 +31,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
   const int64_t gl = g < nreal ? g : nreal - 1;
   const uint4 a = x[gl * 8 + part * 2];
   const uint4 b = x[gl * 8 + part * 2 + 1];
-  float v[16];
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f16x2 h = h2_from_u32(w[i]);
-    v[2 * i] = (float)h.x;
-    v[2 * i + 1] = (float)h.y;
-  }
+  const f16x8 v[2] = {__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b)};
   uint32_t packed[2];
   uint32_t p = GroupQ<kQLanes>::run(v, packed);
   if (g < ngroups) {
