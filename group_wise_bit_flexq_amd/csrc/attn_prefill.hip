@@ -62,6 +62,14 @@ __device__ __forceinline__ int k_off(int row, int ch) {
   else return row * HD + ((ch ^ ((row >> 1) & 7)) << 3);
 }
 
+// Lane l receives x of lanes l % 32 and 32 + l % 32 (v_permlane32_swap): the two
+// halves of a query's statistics, in the same order on both lanes that hold them.
+__device__ __forceinline__ void lane_halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restrict__ qkv, int S,
                                                            int nh, int b0, KVView kv,
@@ -115,17 +123,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   float m_run = -INFINITY, l_run = 0.0f;
 
   // staging: thread t copies chunks c = t + 256 u of the block's K and V rows
-  // (row c / HC, chunk c % HC); keys past S read row S - 1 and are masked.  The
-  // registers are named scalars (arrays of them would live in scratch memory).
+  // (row c / HC, chunk c % HC) through a raw buffer view of the block's rows that ends
+  // at key S - 1: the per-lane offsets are fixed, the block moves the view's base, and
+  // keys past S read zeros (they are masked).  The registers are named scalars (arrays
+  // of them would live in scratch memory).
   static_assert(CPT == 2 || CPT == 4, "staging copies are stamped out for 2 or 4 per thread");
   uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
-#define PF_LD(u, KB_)                                                           \
-  if constexpr ((u) < CPT) {                                                    \
-    const int _c = tid + 256 * (u);                                             \
-    const int _key = min((KB_) * KB + _c / HC, S - 1);                          \
-    const f16* _row = base + (int64_t)_key * ld + head * HD + (_c % HC) * 8;    \
-    rk##u = *(const uint4*)(_row + h);                                          \
-    rv##u = *(const uint4*)(_row + 2 * h);                                      \
+  int voff0 = 0, voff1 = 0, voff2 = 0, voff3 = 0;
+#define PF_OFF(u)                                                                          \
+  if constexpr ((u) < CPT) {                                                               \
+    const int _c = tid + 256 * (u);                                                        \
+    voff##u = ((_c / HC) * (int)ld + head * HD + (_c % HC) * 8) * (int)sizeof(f16);       \
+  }
+  PF_OFF(0) PF_OFF(1) PF_OFF(2) PF_OFF(3)
+#undef PF_OFF
+#define PF_LD(u, RS_)                                                                      \
+  if constexpr ((u) < CPT) {                                                               \
+    rk##u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(               \
+        RS_, voff##u, h * (int)sizeof(f16), 0));                                           \
+    rv##u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(               \
+        RS_, voff##u, 2 * h * (int)sizeof(f16), 0));                                       \
   }
 #define PF_ST(u, ST_)                                                           \
   if constexpr ((u) < CPT) {                                                    \
@@ -134,7 +151,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
     *(uint4*)(sK + (ST_) * P::K_STAGE + k_off<HD>(_r, _ch)) = rk##u;            \
     *(uint4*)(sV + (ST_) * P::V_STAGE + _r * VLD + _ch * 8) = rv##u;            \
   }
-#define LOAD_KV(KB_) do { PF_LD(0, KB_) PF_LD(1, KB_) PF_LD(2, KB_) PF_LD(3, KB_) } while (0)
+#define LOAD_KV(KB_)                                                                       \
+  do {                                                                                     \
+    const int _k0 = (KB_) * KB;                                                            \
+    const rsrc_t _rs = make_rsrc(base + (int64_t)_k0 * ld, min(S - _k0, KB) * (int)ld * 2); \
+    PF_LD(0, _rs) PF_LD(1, _rs) PF_LD(2, _rs) PF_LD(3, _rs)                                \
+  } while (0)
 #define STORE_KV(ST_) do { PF_ST(0, ST_) PF_ST(1, ST_) PF_ST(2, ST_) PF_ST(3, ST_) } while (0)
 
   // transposing-read lane geometry: 16-lane group a = lane / 16 covers dims
@@ -190,7 +212,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mb = fmaxf(mb, s[t][r]);
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64)) * scale_log2;
+      {
+        float lo, hi;
+        lane_halves(mb, lo, hi);
+        mb = fmaxf(lo, hi) * scale_log2;
+      }
       // Lazy rescaling: the reference point m_run only moves when the block max exceeds
       // it by more than 8 (probabilities stay <= 2^8, far inside fp16's range and at
       // the same relative precision); otherwise O and l keep their scale.
@@ -219,8 +245,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
           ls += p;
           pf[2 * t + (r >> 3)][r & 7] = (f16)p;
         }
-      ls += __shfl_xor(ls, 32, 64);
-      l_run += ls;
+      {
+        float lo, hi;
+        lane_halves(ls, lo, hi);
+        l_run += lo + hi;
+      }
       // O^T += V^T P^T over the four 16-key steps
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
@@ -263,10 +292,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   constexpr int GPT = HD / 64;                     // groups per token vector
   constexpr int NGROUPS = QB * GPT * 2;            // K and V
   // 4 lanes per 64-element group (16 elements each, two 16-B chunks): a wave
-  // quantizes 16 groups per pass
+  // quantizes 16 groups per pass.  The passes are unrolled, so whether a pass holds K
+  // or V (the first half of the passes is K) is known at compile time.
+  constexpr int kPasses = NGROUPS / 64;
   const int sub = tid & 3;
-  for (int gi = tid >> 2; gi < NGROUPS; gi += 64) {
-    const int isv = gi / (QB * GPT);
+#pragma unroll
+  for (int it = 0; it < kPasses; ++it) {
+    const int gi = (tid >> 2) + 64 * it;
+    const bool isv = it >= kPasses / 2;
     const int rem = gi % (QB * GPT);
     const int tr = rem / GPT;                      // position within the 128
     const int grp = rem % GPT;
@@ -311,6 +344,8 @@ extern "C" int flexq_attn_prefill(const uint16_t* qkv, int32_t B, int32_t S, int
       ((uintptr_t)kv->pad & 3))
     return FLEXQ_ERR_INVALID;
   if (kv->heads > 65535 || B > 65535) return FLEXQ_ERR_UNSUPPORTED;
+  // a key block (64 rows of q, k, v) is addressed with 32-bit byte offsets
+  if ((int64_t)64 * 3 * kv->heads * kv->head_dim * 2 >= ((int64_t)1 << 31)) return FLEXQ_ERR_UNSUPPORTED;
   KVView v{kv->k_codes, kv->v_codes, (uint32_t*)kv->k_params, (uint32_t*)kv->v_params, kv->heads,
            kv->max_len};
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kv->head_dim);
