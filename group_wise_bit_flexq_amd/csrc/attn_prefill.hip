@@ -288,41 +288,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const f16* __restr
   }
 
   // 4-bit store of K and V for positions [q0, q0 + 128) from the staged tiles (key
-  // block 2 qb + i sits in stage i; the last block's stores preceded the last barrier)
+  // block 2 qb + i sits in stage i; the last block's stores preceded the last barrier).
+  // One lane per 64-element group: thread t quantizes group t % GPT of position
+  // t / GPT, first of K, then of V, so no group statistic is computed twice and no
+  // lanes exchange anything; the two groups of a position sit in adjacent lanes and a
+  // wave writes whole cache lines of codes.
   constexpr int GPT = HD / 64;                     // groups per token vector
-  constexpr int NGROUPS = QB * GPT * 2;            // K and V
-  // 4 lanes per 64-element group (16 elements each, two 16-B chunks): a wave
-  // quantizes 16 groups per pass.  The passes are unrolled, so whether a pass holds K
-  // or V (the first half of the passes is K) is known at compile time.
-  constexpr int kPasses = NGROUPS / 64;
-  const int sub = tid & 3;
-#pragma unroll
-  for (int it = 0; it < kPasses; ++it) {
-    const int gi = (tid >> 2) + 64 * it;
-    const bool isv = it >= kPasses / 2;
-    const int rem = gi % (QB * GPT);
-    const int tr = rem / GPT;                      // position within the 128
-    const int grp = rem % GPT;
+  static_assert(QB * GPT <= 256, "one group per thread and pass");
+  if (tid < QB * GPT) {
+    const int tr = tid / GPT;                      // position within the 128
+    const int grp = tid % GPT;
     const int tok = q0 + tr;
     const int stg = tr / KB, row = tr % KB;
-    const int ch = grp * 8 + sub * 2;
-    f16x8 xa, xb;
-    if (isv) {
-      xa = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8);
-      xb = *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + ch * 8 + 8);
-    } else {
-      xa = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch));
-      xb = *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, ch + 1));
-    }
-    const f16x8 x[2] = {xa, xb};
-    uint32_t packed[2];
-    const uint32_t prm = GroupQ<4>::run(x, packed);
-    if (tok < S) {
-      const int64_t slot = ((int64_t)(b0 + b) * kv.nh + head) * kv.max_len + tok;
-      uint8_t* cbase = isv ? kv.vc : kv.kc;
-      uint32_t* pbase = isv ? kv.vp : kv.kp;
-      *(uint2*)(cbase + slot * (HD / 2) + grp * 32 + sub * 8) = make_uint2(packed[0], packed[1]);
-      if (sub == 0) pbase[slot * GPT + grp] = prm;
+    const int64_t slot = ((int64_t)(b0 + b) * kv.nh + head) * kv.max_len + tok;
+#pragma unroll
+    for (int isv = 0; isv < 2; ++isv) {
+      f16x8 x[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        x[c] = isv ? *(const f16x8*)(sV + stg * P::V_STAGE + row * VLD + (grp * 8 + c) * 8)
+                   : *(const f16x8*)(sK + stg * P::K_STAGE + k_off<HD>(row, grp * 8 + c));
+      uint32_t packed[8];
+      const uint32_t prm = GroupQ<1>::run(x, packed);
+      if (tok < S) {
+        uint4* cdst = (uint4*)((isv ? kv.vc : kv.kc) + slot * (HD / 2) + grp * 32);
+        cdst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        cdst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+        (isv ? kv.vp : kv.kp)[slot * GPT + grp] = prm;
+      }
     }
   }
 }

@@ -1,7 +1,7 @@
 // Device-side group quantizer shared by the standalone quantize kernel, the prefill
 // attention's KV store and the decode attention's append.
 //
-// A 64-element group is held by LPG consecutive lanes (LPG = 4 or 8), each lane
+// A 64-element group is held by LPG consecutive lanes (LPG = 1, 4 or 8), each lane
 // holding E = 64 / LPG consecutive elements.  Arithmetic follows the compression
 // step of the FlexGen walkthrough, section 6.3 (4 bits, group 64, asymmetric
 // min/max), in fp32 with a fixed sequence so that codes are reproducible:
@@ -33,7 +33,7 @@ __device__ __forceinline__ float sub_half(uint32_t pair, int hi, float c) {
 
 template <int LPG>
 struct GroupQ {
-  static_assert(LPG == 4 || LPG == 8, "4 or 8 lanes per group");
+  static_assert(LPG == 1 || LPG == 4 || LPG == 8, "1, 4 or 8 lanes per group");
   static constexpr int E = 64 / LPG;
   static constexpr int W = E / 8;     // 8-element vectors (and packed code words) per lane
 
@@ -57,8 +57,10 @@ struct GroupQ {
       }
     f16x2 mm = (f16x2){__builtin_elementwise_minimum(lo.x, lo.y),
                        -__builtin_elementwise_maximum(hi.x, hi.y)};
-    mm = __builtin_elementwise_minimum(mm, h2_from_u32(dpp_u32<0xB1>(u32_from_h2(mm))));
-    mm = __builtin_elementwise_minimum(mm, h2_from_u32(dpp_u32<0x4E>(u32_from_h2(mm))));
+    if constexpr (LPG >= 4) {
+      mm = __builtin_elementwise_minimum(mm, h2_from_u32(dpp_u32<0xB1>(u32_from_h2(mm))));
+      mm = __builtin_elementwise_minimum(mm, h2_from_u32(dpp_u32<0x4E>(u32_from_h2(mm))));
+    }
     if constexpr (LPG == 8)
       mm = __builtin_elementwise_minimum(mm, h2_from_u32(dpp_u32<0x141>(u32_from_h2(mm))));
     const float mn = (float)mm.x, mx = -(float)mm.y;
