@@ -3,6 +3,9 @@
     python -m group_wise_bit_flexq_amd.kernel_probe gemm --workload opt175b --reps 2
         the four prefill 4-bit GEMMs of one decoder layer (M = micro-batch x prompt
         rows), launched exactly as the model path launches them;
+    python -m group_wise_bit_flexq_amd.kernel_probe gemm_vs_library --workload opt175b --reps 2
+        the same four GEMMs beside torch.mm (the vendor library's fp16 GEMM) on the
+        dequantized weights, alternated in one process;
     python -m group_wise_bit_flexq_amd.kernel_probe decode --workload opt175b --reps 2
         one decode step's 4-bit GEMMs (M = batch) and decode attention over a cache
         of prompt + gen/2 positions;
@@ -83,6 +86,37 @@ def gemm(wl, reps, rows):
                                        out=y, ws=ws), reps)
         res[name] = {"M": rows, "N": n, "K": k, "ms": ms, "tflops": 2 * rows * n * k / ms / 1e9}
         del x, y, ws
+    return res
+
+
+def gemm_vs_library(wl, reps, rows, rounds=3):
+    """The prefill GEMMs beside the vendor library's plain fp16 GEMM on the same shapes
+    (torch.mm, i.e. hipBLASLt, on the dequantized weights: what the 4-bit GEMM would
+    cost if the weights were kept in fp16), alternated in one process."""
+    import torch
+
+    from group_wise_bit_flexq_amd import flexq as F
+    from group_wise_bit_flexq_amd import synth
+    h, f = wl.hidden, wl.ffn
+    w16 = synth.layer_weights_fp16(h, f, 0, 0, device="cuda")
+    L = F.QLayer.from_fp16(w16, wl.heads)
+    shapes = {"wqkv": (3 * h, h), "wo": (h, h), "w1": (f, h), "w2": (h, f)}
+    res = {name: {"M": rows, "N": n, "K": k, "w4_ms": [], "fp16_library_ms": []}
+           for name, (n, k) in shapes.items()}
+    for _ in range(rounds):
+        for name, (n, k) in shapes.items():
+            x = synth.normal_fp16((rows, k), 1.0, 1, device="cuda")
+            y = torch.empty(rows, n, dtype=torch.float16, device="cuda")
+            ws = torch.empty(max(F.linear_ws_bytes(rows, n, k), 16), dtype=torch.uint8,
+                             device="cuda")
+            res[name]["w4_ms"].append(_time(lambda: F.linear_w4(x, L.m[name], out=y, ws=ws), reps))
+            wd = F.dequantize(F.quantize(w16[name]))     # [n][k] fp16: the same codes
+            res[name]["fp16_library_ms"].append(_time(lambda: torch.mm(x, wd.t(), out=y), reps))
+            del x, y, ws, wd
+    for name, r in res.items():
+        fl = 2.0 * r["M"] * r["N"] * r["K"]
+        r["w4_tflops"] = fl / min(r["w4_ms"]) / 1e9
+        r["fp16_library_tflops"] = fl / min(r["fp16_library_ms"]) / 1e9
     return res
 
 
@@ -317,7 +351,7 @@ def copy(mib, reps):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("what", choices=["gemm", "decode", "sparse", "host_attn", "host_tier",
+    ap.add_argument("what", choices=["gemm", "gemm_vs_library", "decode", "sparse", "host_attn", "host_tier",
                                      "prefill_attn", "quant", "quant_ex", "stress", "pick",
                                      "mfma", "copy"])
     ap.add_argument("--threads", type=int, default=16)
@@ -331,6 +365,8 @@ def main():
     wl = WORKLOADS[a.workload]
     if a.what == "gemm":
         r = gemm(wl, a.reps, wl.micro_batch * wl.prompt)
+    elif a.what == "gemm_vs_library":
+        r = gemm_vs_library(wl, a.reps, wl.micro_batch * wl.prompt)
     elif a.what == "decode":
         r = decode(wl, a.reps)
     elif a.what == "host_tier":
