@@ -76,9 +76,10 @@ struct GroupQ {
 
     // t = fl32(fl32(x - min) * inv) lies in [0, 15.008] whenever the step is a normal
     // fp16 (its rounding error is below 2^-11), so the clamp is needed only for a
-    // subnormal step.  rne(t) is taken by adding 2^23: the sum's low mantissa bits are
-    // the code, and its exponent bits, shifted with each code, sum to 0xFB000000
-    // modulo 2^32 over a word, which the start value 0x05000000 cancels.
+    // subnormal step.  v_cvt_pk_u8_f32 rounds to nearest even (checked on the chip
+    // over every tie in [0, 16)) and drops rne(t) into one byte of a word: even codes
+    // into the bytes of `lo`, odd codes into those of `hi`, and lo | hi << 4 is the
+    // packed word (code i in bits 4i .. 4i + 3).
     const bool tiny = bits_from_h(s16) != 0 && (bits_from_h(s16) & 0x7C00) == 0;
     float t[E];
 #pragma unroll
@@ -93,10 +94,13 @@ struct GroupQ {
     }
 #pragma unroll
     for (int v = 0; v < W; ++v) {
-      uint32_t word = 0x05000000u;
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) word += __builtin_bit_cast(uint32_t, t[8 * v + i] + 0x1p23f) << (4 * i);
-      packed[v] = word;
+      for (int k = 0; k < 4; ++k) {
+        lo = __builtin_amdgcn_cvt_pk_u8_f32(t[8 * v + 2 * k], k, lo);
+        hi = __builtin_amdgcn_cvt_pk_u8_f32(t[8 * v + 2 * k + 1], k, hi);
+      }
+      packed[v] = lo | (hi << 4);
     }
     const f16 off = (f16)(mn == 0.0f ? 0.0f : mn);
     return (uint32_t)bits_from_h(off) | ((uint32_t)bits_from_h(s16) << 16);
