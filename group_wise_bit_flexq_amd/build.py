@@ -42,11 +42,17 @@ def _sources():
                   if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+# per-source additions: decode attention's K pass accumulates one small MFMA chain per
+# token step and reads it at once, so its accumulators belong in ordinary VGPRs
+# (the default heuristic puts them in AGPRs and copies them back every step)
+EXTRA_CFLAGS = {"attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     base, ext = os.path.splitext(os.path.basename(src))
     obj = os.path.join(BUILD, base + (".o" if ext == ".hip" else ".host.o"))
     if ext == ".hip":
-        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *EXTRA_CFLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     else:
         cmd = [CLANGXX, *HOST_CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

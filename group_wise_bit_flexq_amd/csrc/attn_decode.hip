@@ -223,22 +223,33 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
 
   const int j = lane % LPT;       // this lane's 32 dims: 32 j .. 32 j + 31 (group j / 2)
   const int grp = j >> 1;
+  // K-pass lane map.  With head_dim 128 the dot products go to the matrix cores: lane l
+  // holds dims 32 (l / 16) .. +31 of token l % 16 of its wave step, which is the B
+  // operand of v_mfma_f32_16x16x32_f16 (k-chunk l / 16, column l % 16); head_dim 64
+  // keeps v_dot2 with the V pass's map.
+  constexpr bool kMfK = HD == 128;
+  const int jk = kMfK ? (lane >> 4) : j;
+  const int tk = kMfK ? (lane & 15) : lane / LPT;
   // q and the first batch of K go out before the append: none of these loads can read
   // position pos unless the first batch reaches it (then the batch waits for the append)
   uint4 qraw[4];
   {
-    const uint4* qp = (const uint4*)(row + head * HD + 32 * j);
+    const uint4* qp = (const uint4*)(row + head * HD + 32 * jk);
 #pragma unroll
     for (int c = 0; c < 4; ++c) qraw[c] = qp[c];
   }
   u32x4 cw[UNR];
   uint32_t prm[UNR];
+  u32x2 kprm[UNR];   // matrix-core K pass: the (offset, scale) words of both groups
   auto load_k = [&](int tb) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int t = tb + u * TPB + wave * TPW + lane / LPT;   // >= t_end: zeros
-      cw[u] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, t * (HD / 2) + 16 * j, 0, 0);
-      prm[u] = __builtin_amdgcn_raw_buffer_load_b32(kp_rs, (t * GPT + grp) * 4, 0, 0);
+      const int t = tb + u * TPB + wave * TPW + tk;   // >= t_end: zeros
+      cw[u] = __builtin_amdgcn_raw_buffer_load_b128(k_rs, t * (HD / 2) + 16 * jk, 0, 0);
+      if constexpr (kMfK)
+        kprm[u] = __builtin_amdgcn_raw_buffer_load_b64(kp_rs, t * GPT * 4, 0, 0);
+      else
+        prm[u] = __builtin_amdgcn_raw_buffer_load_b32(kp_rs, (t * GPT + grp) * 4, 0, 0);
     }
   };
   const bool k_early = t_begin < t_end && (t_end < T || t_begin + UNR * TPB <= pos);
@@ -291,6 +302,32 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   // 2^24 of the subnormal codes) and into the sum of q for the offset term
   const float ks = 16777216.0f * scale_log2;
   const float qsum_s = qsum * scale_log2;
+  // matrix-core K pass.  A word's codes enter as fp16 subnormals, as in the v_dot2
+  // pass: even dims c 2^-24 from the low nibbles, odd dims 16 c 2^-24 from the high
+  // nibbles left in place, in the order (d0, d2, d4, d6, d1, d3, d5, d7).  A operand
+  // rows: 0 = q of group 0's even dims (k-chunks 0, 1; zeros in the odd slots), 1 = the
+  // same for group 1 (k-chunks 2, 3), 2 and 3 = the odd dims of groups 0 and 1; every
+  // other row is zero.  C rows 0..3 of a token then hold exact-product sums whose odd
+  // rows carry a factor 16.  qg0, qg1: the groups' sums of q.
+  f16x8 aq[4];
+  float qg0 = 0.0f, qg1 = 0.0f;
+  if constexpr (kMfK) {
+    const int arow = lane & 15, grp_k = jk >> 1;
+    const bool even_row = arow == grp_k, odd_row = arow == 2 + grp_k;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16 z = (f16)0.0f;
+      const f16x8 ve = {qe[2 * k].x, qe[2 * k].y, qe[2 * k + 1].x, qe[2 * k + 1].y, z, z, z, z};
+      const f16x8 vo = {z, z, z, z, qo[2 * k].x, qo[2 * k].y, qo[2 * k + 1].x, qo[2 * k + 1].y};
+      aq[k] = even_row ? ve : (odd_row ? vo : (f16x8){});
+    }
+    // lanes of 16-lane row r hold the sum of dims 32 r .. 32 r + 31
+    const float pair = qsum + __shfl_xor(qsum, 16, 64);   // rows 0, 1: group 0; 2, 3: group 1
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair), __float_as_uint(pair),
+                                                    false, false);
+    qg0 = __uint_as_float(r[0]) * scale_log2;
+    qg1 = __uint_as_float(r[1]) * scale_log2;
+  }
 
   // ---- 2. K pass, UNR block steps per iteration: every load of the iteration is
   // issued before the first use (positions past the split's end read zeros and their
@@ -301,8 +338,34 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
     if (!k_early || tb != t_begin) load_k(tb);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int t = tb + u * TPB + wave * TPW + lane / LPT;
+      const int t = tb + u * TPB + wave * TPW + tk;
       const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
+      if constexpr (kMfK) {
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = w[k] & 0xF0F0F0F0u;
+          const uint32_t b0 = __builtin_amdgcn_perm(lo, lo, 0x0c010c00u);
+          const uint32_t b1 = __builtin_amdgcn_perm(lo, lo, 0x0c030c02u);
+          const uint32_t b2 = __builtin_amdgcn_perm(hi, hi, 0x0c010c00u);
+          const uint32_t b3 = __builtin_amdgcn_perm(hi, hi, 0x0c030c02u);
+          const f16x8 b = __builtin_bit_cast(f16x8, (u32x4){b0, b1, b2, b3});
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[k], b, c, 0, 0, 0);
+        }
+        // lanes 0..15 (token tk): group g's sum of q . c is 2^24 (c[g] + c[2 + g] / 16)
+        const float m0 = (float)h_from_bits(kprm[u].x & 0xFFFFu);
+        const float s0 = (float)h_from_bits(kprm[u].x >> 16);
+        const float m1 = (float)h_from_bits(kprm[u].y & 0xFFFFu);
+        const float s1 = (float)h_from_bits(kprm[u].y >> 16);
+        const float d0 = __builtin_fmaf(c[2], 0.0625f, c[0]);
+        const float d1 = __builtin_fmaf(c[3], 0.0625f, c[1]);
+        const float partial = (s0 * ks) * d0 + (s1 * ks) * d1 + (m0 * qg0 + m1 * qg1);
+        if (lane < 16 && t < t_end) {
+          mx_run = fmaxf(mx_run, partial);
+          sc[t - t_begin] = partial;
+        }
+        continue;
+      }
       // code pairs as fp16 subnormals: even dims c * 2^-24 from the low nibbles, odd
       // dims 16 c * 2^-24 from the high nibbles left in place (exact products; the
       // odd-dim sum is scaled by 1/16 once per token)
