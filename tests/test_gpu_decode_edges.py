@@ -124,3 +124,29 @@ def test_decode_append_edge_groups(B, nh, hd, pos):
     delta = hd * 2.0**-23 * sabs
     extra = (vmax * (2.0**-16 + 4 * delta))[:, :, None] * np.ones((1, 1, hd))
     assert_close_fp16(out, ref, extra=extra.reshape(B, h), what="decode over edge groups")
+
+
+@pytest.mark.parametrize("B,S,nh,hd", [(2, 200, 3, 64), (2, 300, 3, 128), (1, 128, 8, 128)])
+def test_prefill_store_edge_groups(B, S, nh, hd):
+    """The prefill kernel's fused 4-bit store (one lane per 64-element group) turns K and
+    V rows made of the quantizer's special groups into the oracle's codes and (offset,
+    scale) bit for bit.  q = 0 makes every score 0, so the output is the plain causal
+    mean of V and is checked within the usual prefill bound."""
+    F = require_gpu()
+    _say("prefill store edges", B, S, nh, hd)
+    rng = np.random.default_rng(B * S + nh + hd)
+    h = nh * hd
+    qkv = np.zeros((B * S, 3 * h), F16)
+    qkv[:, h:2 * h] = _edge_groups(rng, B * S * h // 64).reshape(B * S, h)
+    qkv[:, 2 * h:] = _edge_groups(rng, B * S * h // 64).reshape(B * S, h)
+    qkv[:, 2 * h:][np.abs(qkv[:, 2 * h:].astype(np.float64)) > 1e3] *= F16(1e-3)   # modest |v|
+    kv = F.KV4(B, nh, hd, S)
+    out = to_np(F.attn_prefill(torch.from_numpy(qkv).cuda(), B, S, kv))
+    torch.cuda.synchronize()
+    oc = O.KVCache(B, nh, hd, S)
+    ref = O.attn_prefill(qkv, B, S, nh, hd, oc)
+    for name in ("k_codes", "v_codes", "k_params", "v_params"):
+        a, b = to_np(getattr(kv, name)), getattr(oc, name)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), name
+    vmax = np.abs(qkv[:, 2 * h:].astype(np.float64)).max()
+    assert_close_fp16(out, ref, extra=2.0**-10 * vmax, what="prefill over edge groups")
