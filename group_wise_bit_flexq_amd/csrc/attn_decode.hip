@@ -9,8 +9,10 @@
 //  1. the split that ends at `pos` first quantizes this step's k and v (8 lanes per
 //     64-element group) and appends them at position pos;
 //  2. K pass: score_t = sum_g [ s_g * sum_d q_d c_td + m_g * sum_d q_d ]  (the
-//     dequantized key c*s+m never materialises).  Codes enter v_dot2_f32_f16 as fp16
-//     subnormals c * 2^-24, so every product is exact and the 2^24 is folded into s;
+//     dequantized key c*s+m never materialises).  Codes enter as fp16 subnormals
+//     c * 2^-24, so every product is exact and the 2^24 is folded into s; with
+//     head_dim 128 the sums run on the matrix cores (q as a 4-row A operand), with 64
+//     in v_dot2_f32_f16;
 //  3. softmax over the split in fp32: the maximum is kept during the K pass, then one
 //     pass over the scores in LDS turns them into weights and sums them;
 //  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs fed two exact fp16

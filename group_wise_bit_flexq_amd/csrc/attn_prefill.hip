@@ -21,7 +21,7 @@
 //    each 16-lane group, lane j points at 4 dims of key j / 4 and lane i receives
 //    dim i of the 4 keys.
 // After the loop the work-group quantizes K and V of its own 128 positions into the
-// cache (4 lanes per 64-element group), reading them from the staged LDS tiles.
+// cache (one lane per 64-element group), reading them from the staged LDS tiles.
 // Left padding (the generation loop's attention mask): keys below the sequence's pad
 // count are masked, key blocks wholly below it are skipped (except the work-group's
 // own two, which the store needs staged), and a query with no visible key writes 0.
