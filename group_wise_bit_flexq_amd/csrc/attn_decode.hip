@@ -459,15 +459,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
         const float p = live ? sc[rel[u]] : 0.0f;
         const float m = (float)h_from_bits(prm[u] & 0xFFFFu);
         const float s = (float)h_from_bits(prm[u] >> 16);
-        const float ps = p * s;
+        // the codes enter as fp16 subnormals c 2^-24 (even dims, low nibbles) and
+        // 16 c 2^-24 (odd dims, high nibbles in place), two per byte permute; 2^24 is
+        // folded into the weight, so even-dim products are exactly p s c and odd-dim
+        // ones exactly 16 p s c (the odd accumulators are scaled by 1/16 after the pass)
+        const float ps = p * s * 16777216.0f;
         pm += p * m;
         const uint32_t w[4] = {cw[u].x, cw[u].y, cw[u].z, cw[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          // two exact fp16 codes per convert; each feeds an fp32 FMA (v_fma_mix_f32)
-          const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = (w[k] >> 4) & 0x0F0F0F0Fu;
-          const f16x2 e02 = code_pair_f16<false>(lo), e46 = code_pair_f16<true>(lo);
-          const f16x2 e13 = code_pair_f16<false>(hi), e57 = code_pair_f16<true>(hi);
+          const uint32_t lo = w[k] & 0x0F0F0F0Fu, hi = w[k] & 0xF0F0F0F0u;
+          const f16x2 e02 = h2_from_u32(__builtin_amdgcn_perm(lo, lo, 0x0c010c00u));
+          const f16x2 e46 = h2_from_u32(__builtin_amdgcn_perm(lo, lo, 0x0c030c02u));
+          const f16x2 e13 = h2_from_u32(__builtin_amdgcn_perm(hi, hi, 0x0c010c00u));
+          const f16x2 e57 = h2_from_u32(__builtin_amdgcn_perm(hi, hi, 0x0c030c02u));
           acc[8 * k + 0] = __builtin_fmaf(ps, (float)e02.x, acc[8 * k + 0]);
           acc[8 * k + 1] = __builtin_fmaf(ps, (float)e13.x, acc[8 * k + 1]);
           acc[8 * k + 2] = __builtin_fmaf(ps, (float)e02.y, acc[8 * k + 2]);
@@ -486,6 +491,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const f16* __restrict_
   } else {
     v_pass(std::false_type{});
   }
+#pragma unroll
+  for (int e = 1; e < 32; e += 2) acc[e] *= 0.0625f;   // odd dims carried a factor 16
   // lanes of one 16-lane row that own the same dims (lane = LPT * token + j) are summed
   // with DPP rotations; each row's sums go to LDS for the output step
 #pragma unroll
