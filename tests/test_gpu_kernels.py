@@ -131,7 +131,13 @@ def _bound_linear(x, w16, K):
                                    (100, 200, 64), (144, 64, 4096),
                                    (144, 33792, 4096), (97, 33792, 2048),   # decode kernel, two splits
                                    (160, 128, 128),
-                                   (300, 256, 640), (513, 192, 1024), (4, 256, 8192)])
+                                   (300, 256, 640), (513, 192, 1024), (4, 256, 8192),
+                                   # k-loop remainders: large-M kernel with an odd k-tile
+                                   # count (9; 45 in 5 splits of 9), small-M kernel with 7,
+                                   # decode kernel with 4 and 3 left after its 5-stage
+                                   # groups (M x N not a multiple of 4 keeps K unsplit)
+                                   (400, 320, 576), (300, 256, 2880), (41, 250, 448),
+                                   (143, 382, 576), (121, 254, 512)])
 @pytest.mark.parametrize("epi", ["plain", "bias_relu", "bias_res"])
 def test_linear_w4(M, N, K, epi):
     F = require_gpu()
