@@ -219,7 +219,8 @@ def check_embedding(wl, rec, head):
 
 
 def check_head(wl, rec, head):
-    """Logits of the recorded steps from the recorded last hidden state (the benchmark spec bounds),
+    """Logits of the recorded steps from the recorded last hidden state (max-abs 2e-2,
+    relative Frobenius 1e-2),
     and every greedy token: identical to the oracle's argmax unless the oracle's own top-2
     gap at that step is within twice the measured logit error (a near-tie).  Returns the
     number of near-ties."""
