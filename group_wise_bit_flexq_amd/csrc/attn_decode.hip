@@ -15,8 +15,8 @@
 //     in v_dot2_f32_f16;
 //  3. softmax over the split in fp32: the maximum is kept during the K pass, then one
 //     pass over the scores in LDS turns them into weights and sums them;
-//  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs fed two exact fp16
-//     codes per convert;
+//  4. V pass: o_d = sum_t p_t s_t c_td + sum_t p_t m_t, fp32 FMAs (v_fma_mix) reading
+//     the codes as fp16 subnormals, two per byte permute, as in the K pass;
 //  5. with several splits, each writes (max, sum, o[]) and a merge kernel rescales
 //     and adds them in split order.
 // The K and V rows of one (sequence, head) are read through raw buffer views that end
