@@ -2,19 +2,22 @@
 //
 // The pages' linear layers are fp16 matmuls whose weights are stored compressed
 // (FlexGen walkthrough, section 6.3: weights grouped along the input dimension,
-// 64 per group, 4 bits, fp16 parameters).  Two kernels share the arithmetic:
+// 64 per group, 4 bits, fp16 parameters).  Three kernels share the arithmetic:
 //
 //  * large M (prefill, M = 48 x 512): 256 x 256 x 64 tiles, 8 waves.  The weight
 //    tile is expanded to fp16 on its way into LDS (v_pk_fma_f16: one rounding of
 //    c * scale + offset), once per work-group and k-step, and reused by all 256 rows;
-//  * small M (decode, M = batch <= 160): weights are streamed once, straight into
-//    the registers of the wave that uses them, and dequantized there; only the
+//  * decode batches (64 < M <= 144): every operand goes straight from memory into a
+//    5-stage LDS ring (buffer loads with the LDS flag); each wave expands only its
+//    own weight columns, in registers, so every weight is read and expanded once;
+//  * other small M (M <= 64, 144 < M <= 160): weight codes are streamed straight
+//    into the registers of the wave that uses them and expanded there; only the
 //    activation tile goes through LDS.
 //
-// Both feed v_mfma_f32_32x32x16_f16 (fp16 operands, fp32 accumulators) and finish
-// with a fused bias / ReLU / residual epilogue and a single fp16 rounding.  Where a
-// shape has too few tiles for 256 CUs, K is split and a second kernel adds the fp32
-// partial sums in split order (deterministic).
+// All feed the matrix cores with fp16 operands and fp32 accumulators and finish with
+// a fused bias / ReLU / residual epilogue and a single fp16 rounding.  Where a shape
+// has too few tiles for the CUs, K is split and a second kernel adds the fp32 partial
+// sums in split order (deterministic).
 #include "common.h"
 
 namespace flexq {
