@@ -54,18 +54,19 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
 
 def _time(fn, reps):
+    """Average time of one call, from `reps` calls launched back to back between two
+    events: the host's per-call argument handling overlaps the previous call's kernels,
+    as it does in the generation loop, instead of being timed as GPU idle time."""
     import torch
     fn()
     torch.cuda.synchronize()
-    ts = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
         fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    return sum(ts) / len(ts)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def gemm(wl, reps, rows):
