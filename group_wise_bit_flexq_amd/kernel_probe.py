@@ -41,7 +41,8 @@
         an elementwise device copy of a known size, the reference that scales the
         HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the probes above, and a
         measured HBM rate (read + write) beside the nominal 8 TB/s.
-Each prints its per-launch times (HIP events) as one JSON line.
+Each prints its per-launch times (HIP events) as one JSON line; --warm S runs the
+calls untimed for about S seconds first (the clock of a GPU that was idle ramps up).
 """
 from __future__ import annotations
 
@@ -53,12 +54,28 @@ import sys
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 
 
+WARM_S = 0.0   # set by --warm
+
+
 def _time(fn, reps):
     """Average time of one call, from `reps` calls launched back to back between two
     events: the host's per-call argument handling overlaps the previous call's kernels,
-    as it does in the generation loop, instead of being timed as GPU idle time."""
+    as it does in the generation loop, instead of being timed as GPU idle time.  With
+    --warm S the calls first run for about S seconds (at most 2000 calls): a GPU that
+    has just been idle runs its first milliseconds of work at a lower clock.  Without
+    it (the default, used by the counter runs) one untimed call precedes the timed ones."""
+    import time
+
     import torch
+    warm_s = WARM_S
     fn()
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < warm_s and n < 2000:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -359,7 +376,11 @@ def main():
     ap.add_argument("--workload", default="opt175b")
     ap.add_argument("--reps", type=int, default=2)
     ap.add_argument("--mib", type=int, default=1024)
+    ap.add_argument("--warm", type=float, default=0.0,
+                    help="seconds of untimed calls before each timed batch (default: one call)")
     a = ap.parse_args()
+    global WARM_S
+    WARM_S = max(a.warm, 0.0)
     from group_wise_bit_flexq_amd import flexq as F
     from group_wise_bit_flexq_amd.workloads import WORKLOADS
     F.lib()
