@@ -98,3 +98,50 @@ def test_quantize_4gib_sampled_rows():
     codes, params = O.quantize(to_np(x[idx]))
     assert np.array_equal(to_np(w.codes[idx]), codes)
     assert np.array_equal(to_np(w.params[idx]).view(np.uint16), params.view(np.uint16))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("hd", [64, 128])
+def test_long_context_split_merge_at_1024_pairs(hd):
+    """Contexts past the 4096-position score buffer with enough (sequence, head) pairs
+    that the context is split only to fit it: batch 16 x 64 heads = 1024 pairs, prompt
+    4200, two decode steps (positions 4200, 4201 -> two splits and the merge).  Sampled
+    pairs followed through prefill (cache bit-exact) and both decode outputs."""
+    F = require_gpu()
+    B, nh, S, steps = 16, 64, 4200, 2
+    h = nh * hd
+    _say("long context split", B, nh, hd, S, steps)
+    assert F.attn_decode_ws_bytes(B, nh, hd, S) > 0   # the split path, not one work-group per pair
+    rng = np.random.default_rng(4200 + hd)
+    kv = F.KV4(B, nh, hd, S + steps)
+    qkv = _stress_qkv(B * S, h, 7 + hd, 0.01, 8.0)
+    att = F.attn_prefill(qkv, B, S, kv)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (B - 1, nh - 1), (int(rng.integers(0, B)), int(rng.integers(0, nh)))]
+    caches = {}
+    for (b, hh) in pairs:
+        small = _head(to_np(qkv[b * S:(b + 1) * S]), hh, hd, h)
+        oc = O.KVCache(1, 1, hd, S + steps)
+        ref = O.attn_prefill(small, 1, S, 1, hd, oc)
+        got = to_np(att[b * S:(b + 1) * S, hh * hd:(hh + 1) * hd])
+        assert_close_fp16(got, ref, extra=2.0**-9 * np.abs(small.astype(np.float64)).max(),
+                          what=f"prefill b={b} h={hh}")
+        for name in ("k_codes", "v_codes"):
+            assert np.array_equal(to_np(getattr(kv, name)[b, hh, :S]), getattr(oc, name)[0, 0, :S])
+        for name in ("k_params", "v_params"):
+            assert np.array_equal(to_np(getattr(kv, name)[b, hh, :S]).view(np.uint16),
+                                  getattr(oc, name)[0, 0, :S].view(np.uint16))
+        caches[(b, hh)] = oc
+    del qkv, att
+    for i in range(steps):
+        pos = S + i
+        q1 = _stress_qkv(B, h, 900 + i, 0.01, 8.0)
+        out = F.attn_decode(q1, pos, kv)
+        torch.cuda.synchronize()
+        qn = to_np(q1)
+        for (b, hh), oc in caches.items():
+            ref = O.attn_decode(_head(qn[b:b + 1], hh, hd, h), pos, oc)
+            got = to_np(out[b:b + 1, hh * hd:(hh + 1) * hd])
+            vmax = 15 * np.abs(oc.v_params[..., 1].astype(np.float64)).max() + \
+                np.abs(oc.v_params[..., 0].astype(np.float64)).max()
+            assert_close_fp16(got, ref, extra=2.0**-16 * vmax, what=f"decode step {i} b={b} h={hh}")
