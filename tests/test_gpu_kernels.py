@@ -137,7 +137,9 @@ def _bound_linear(x, w16, K):
                                    # decode kernel with 4 and 3 left after its 5-stage
                                    # groups (M x N not a multiple of 4 keeps K unsplit)
                                    (400, 320, 576), (300, 256, 2880), (41, 250, 448),
-                                   (143, 382, 576), (121, 254, 512)])
+                                   (143, 382, 576), (121, 254, 512),
+                                   # decode kernel with 6 row tiles of 16 (81 <= M <= 96)
+                                   (90, 384, 512)])
 @pytest.mark.parametrize("epi", ["plain", "bias_relu", "bias_res"])
 def test_linear_w4(M, N, K, epi):
     F = require_gpu()
