@@ -161,7 +161,9 @@ def test_linear_w4(M, N, K, epi):
     assert_close_fp16(got, ref, extra=_bound_linear(x, wd, K) + 1e-7, what=f"linear {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(3, 50272 // 8, 768), (144, 1000, 512), (2, 96, 4096)])
+@pytest.mark.parametrize("M,N,K", [(3, 50272 // 8, 768), (144, 1000, 512), (2, 96, 4096),
+                                   # large-M kernel writing fp32, direct and split-K
+                                   (300, 200, 640), (300, 256, 2048)])
 def test_linear_w4_f32(M, N, K):
     F = require_gpu()
     _say("linear_f32", M, N, K)
